@@ -1,0 +1,155 @@
+/*
+ * nvfp4.h - C ABI of libnvfp4.so, the NVFP4 W4A4 linear on AMD Instinct MI355X (gfx950).
+ *
+ * What the calls compute follows the pages on FastVideo's NVFP4 path, cited by title:
+ *   [DEC]  "minimax_h3_nvfp4_decoder" (API reference of
+ *          fastvideo.models.vaes.minimax_h3_nvfp4_decoder): rotate_activation,
+ *          nvfp4_linear_inference, NVFP4DecoderLinear.
+ *   [CONV] "convert_minimax_h3_text_encoder_nvfp4.py": quantize_language_linear,
+ *          probe_relative_error, main.
+ *   [BLOG] "FastH3-QAD-v2 and NVFP4 VAE Decoders: Better Quality, Faster Decoding,
+ *          and Community LoRAs", section "The whole stack in NVFP4".
+ *
+ * Number formats.  FP4 is E2M1 (magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6; bit 3 is the
+ * sign).  Two codes per byte, the even K index in the low nibble, row-major
+ * [rows][K/2] ([DEC] NVFP4DecoderLinear.from_packed).  One FP8 E4M3 (bias 7,
+ * finite max 448) scale per 16 consecutive K values of a row ([BLOG]).  One fp32
+ * global scale per tensor, gsf = 2688 / max(amax, 1e-12) with 2688 = 6 * 448
+ * ([DEC] NVFP4DecoderLinear._activation_global_sf).  A value v quantizes to
+ *     s    = E4M3_nearest_even_saturating((gsf * bmax) / 6)   (bmax: block max |v|)
+ *     code = E2M1_nearest_even_saturating(v * (gsf / s))      (all codes 0 if s == 0)
+ * every operation in IEEE fp32 round-to-nearest.
+ *
+ * Scale layout.  Block scales are stored k-tile-major: byte (row r, block b) sits at
+ *     ((b / 8) * rows + r) * 8 + (b % 8)
+ * i.e. [ceil(K/128)][rows][8]; a 128-wide K tile of every row is one contiguous run.
+ * Bytes for blocks past K/16 (when K % 128 != 0) are padding and are written as 0.
+ * nvfp4_scale_bytes() gives the size; nvfp4_scale_to_canonical /
+ * nvfp4_scale_from_canonical convert to and from row-major [rows][K/16].
+ *
+ * Memory and streams.  Every pointer named *_dev is device memory owned by the
+ * caller; the library never allocates or frees.  Global scales are fp32 device
+ * scalars, so the dynamic path never waits on the host.  Every call is
+ * asynchronous on `stream` (a hipStream_t; NULL is the default stream); it returns
+ * once its kernels are queued.
+ *
+ * Errors.  Calls return NVFP4_OK (0) or a negative code before anything is queued;
+ * nvfp4_last_error() then gives a message (per calling thread).  Argument checks
+ * mirror the ValueErrors of [DEC] NVFP4DecoderLinear.__init__ and .from_packed.
+ */
+#ifndef NVFP4_H_
+#define NVFP4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_SHAPE = -1,      /* K not a multiple of 16, non-positive sizes, size overflow */
+  NVFP4_ERR_ARG = -2,        /* bad rotation group, dtype, or a required NULL pointer */
+  NVFP4_ERR_WORKSPACE = -3,  /* workspace too small or misaligned */
+  NVFP4_ERR_HIP = -4         /* the HIP runtime refused a launch */
+};
+
+enum { NVFP4_DTYPE_BF16 = 0, NVFP4_DTYPE_F32 = 1 };
+
+#define NVFP4_BLOCK_SIZE 16
+#define NVFP4_SCALE_TILE_K 128
+#define NVFP4_MAX_ROTATION_GROUP 128
+#define NVFP4_WORKSPACE_ALIGN 256
+
+/* Bytes of a block-scale array for a [rows, k] tensor in the layout above. */
+size_t nvfp4_scale_bytes(int64_t rows, int64_t k);
+
+/* Workspace nvfp4_quantize_activation / nvfp4_quantize_weight need (amax partials). */
+size_t nvfp4_quantize_workspace_bytes(void);
+
+/* Workspace nvfp4_linear needs for an [m, k] input: activation codes [m][k/2],
+ * their scales, amax partials and the activation global scale, each 256-byte aligned. */
+size_t nvfp4_linear_workspace_bytes(int64_t m, int64_t k);
+
+/*
+ * rotate_activation ([DEC] rotate_activation(x, group_size); module docstring).
+ * y[r, j*g:(j+1)*g] = x[r, j*g:(j+1)*g] @ (H_g / sqrt(g)), H_g the natural-order
+ * Sylvester Hadamard matrix, computed in fp32 (butterfly strides 1, 2, ..., g/2, then
+ * one multiply by fp32(1/sqrt(g))) and rounded to y_dtype (bf16: nearest even).
+ * x_dev, y_dev: row-major [rows][k] of x_dtype / y_dtype (NVFP4_DTYPE_*); may alias
+ * only if identical and of equal dtype.  group_size: a power of two, 2..128,
+ * dividing k.  bf16 -> bf16 is the activation path; f32 -> bf16 is the weight fold of
+ * [DEC] NVFP4DecoderLinear.from_linear followed by the cast of _packed_weight.
+ */
+int rotate_activation(const void* x_dev, int x_dtype, void* y_dev, int y_dtype,
+                      int64_t rows, int64_t k, int group_size, void* stream);
+
+/*
+ * nvfp4_quantize_weight ([DEC] NVFP4DecoderLinear._packed_weight; [CONV]
+ * quantize_language_linear).  w_dev: bf16 [n][k].  Writes packed_dev [n][k/2],
+ * inv_scale_dev (nvfp4_scale_bytes(n, k), layout above) and *global_sf_w_dev =
+ * 2688 / max(amax(w), 1e-12).  workspace: >= nvfp4_quantize_workspace_bytes().
+ */
+int nvfp4_quantize_weight(const void* w_dev, int64_t n, int64_t k,
+                          uint8_t* packed_dev, uint8_t* inv_scale_dev, float* global_sf_w_dev,
+                          void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/*
+ * nvfp4_quantize_activation: steps 1-3 of [DEC] nvfp4_linear_inference on a bf16
+ * [m][k] input.  rotation_group 0 = none, else x is first rotated as by
+ * rotate_activation (the rotated values are never written).  global_sf_x_dev NULL =
+ * dynamic scale from the amax of the (rotated) input; else the fp32 scale it points
+ * to is used as is (static / unit scale).  Writes codes_dev [m][k/2], scale_dev
+ * (nvfp4_scale_bytes(m, k)) and, if gsf_out_dev is not NULL, the scale used.
+ */
+int nvfp4_quantize_activation(const void* x_dev, int64_t m, int64_t k,
+                              const float* global_sf_x_dev, int rotation_group,
+                              uint8_t* codes_dev, uint8_t* scale_dev, float* gsf_out_dev,
+                              void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/*
+ * nvfp4_gemm: step 4 of [DEC] nvfp4_linear_inference (the mm_fp4 call and the bias
+ * add).  out[i, j] = bf16(alpha * sum_b sx[i,b] sw[j,b] sum_{k in b} qx[i,k] qw[j,k]),
+ * alpha = 1 / (gsf_x * gsf_w) in fp32; then, if bias_dev is not NULL,
+ * out = bf16(out + bias[j]).  Accumulation is fp32 (order unspecified).
+ * x_codes_dev [m][k/2], x_scale_dev (layout above, m rows), packed_dev [n][k/2],
+ * inv_scale_dev (n rows), gsf_x_dev / gsf_w_dev fp32 device scalars,
+ * bias_dev bf16 [n] or NULL, out_dev bf16 [m][n].
+ */
+int nvfp4_gemm(const uint8_t* x_codes_dev, const uint8_t* x_scale_dev, int64_t m, int64_t k,
+               const uint8_t* packed_dev, const uint8_t* inv_scale_dev, int64_t n,
+               const float* gsf_x_dev, const float* gsf_w_dev, const void* bias_dev,
+               void* out_dev, void* stream);
+
+/*
+ * nvfp4_linear ([DEC] nvfp4_linear_inference(x, packed, inv_scale, global_sf_w, bias,
+ * out_features, global_sf_x), preceded by the optional rotation of
+ * NVFP4DecoderLinear.forward).  x_dev: bf16 [m][k] (leading dimensions flattened by
+ * the caller).  packed_dev [out_features][k/2] and inv_scale_dev from
+ * nvfp4_quantize_weight; global_sf_w_dev its fp32 scale.  bias_dev bf16
+ * [out_features] or NULL.  global_sf_x_dev NULL = dynamic activation scale.
+ * rotation_group 0 = none; otherwise the result is bit-identical to
+ * nvfp4_linear(rotate_activation(x, g), ..., 0).  out_dev bf16 [m][out_features].
+ * workspace: >= nvfp4_linear_workspace_bytes(m, k), 256-byte aligned.
+ */
+int nvfp4_linear(const void* x_dev, int64_t m, int64_t k,
+                 const uint8_t* packed_dev, const uint8_t* inv_scale_dev,
+                 const float* global_sf_w_dev, const void* bias_dev, int64_t out_features,
+                 const float* global_sf_x_dev, int rotation_group, void* out_dev,
+                 void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/* Scale-layout conversion: layout above <-> row-major [rows][k/16] bytes. */
+int nvfp4_scale_to_canonical(const uint8_t* layout_dev, uint8_t* canonical_dev,
+                             int64_t rows, int64_t k, void* stream);
+int nvfp4_scale_from_canonical(const uint8_t* canonical_dev, uint8_t* layout_dev,
+                               int64_t rows, int64_t k, void* stream);
+
+/* Message for the last non-zero return on the calling thread ("" if none). */
+const char* nvfp4_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H_ */

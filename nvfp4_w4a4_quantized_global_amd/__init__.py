@@ -1,0 +1,12 @@
+"""NVFP4 W4A4 linear for AMD Instinct MI355X (gfx950).
+
+The arithmetic lives in ``libnvfp4.so`` (hand-written HIP kernels behind the C
+ABI in ``include/nvfp4.h``); this package is its thin torch binding.  Importing
+the package does not load the library; the first call does, and fails loudly if
+it has not been built.
+"""
+from .nvfp4 import (  # noqa: F401
+    MAX_ROTATION_GROUP, NVFP4_BLOCK_SIZE, SCALE_TILE_K, NVFP4Linear, linear_workspace_bytes, nvfp4_gemm,
+    nvfp4_linear, quantize_activation, quantize_weight, quantize_workspace_bytes, rotate_activation, scale_bytes,
+    scale_from_canonical, scale_to_canonical,
+)

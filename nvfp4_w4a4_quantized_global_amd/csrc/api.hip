@@ -1,0 +1,221 @@
+// C ABI of libnvfp4.so: argument checks, workspace carving and kernel launches.
+// The contract of every call is in include/nvfp4.h.  Checks mirror the
+// ValueErrors of NVFP4DecoderLinear.__init__ / .from_packed on the
+// "minimax_h3_nvfp4_decoder" page (in_features divisible by the 16-value block,
+// rotation group dividing in_features, packed weight [out, in/2]).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "../../include/nvfp4.h"
+#include "nvfp4_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return NVFP4_OK;
+  return fail(NVFP4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align_up(size_t v) { return (v + NVFP4_WORKSPACE_ALIGN - 1) / NVFP4_WORKSPACE_ALIGN * NVFP4_WORKSPACE_ALIGN; }
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;   // rows and K each below 2^31
+
+int check_rows_k(const char* fn, int64_t rows, int64_t k, bool allow_empty) {
+  if (rows < 0 || (!allow_empty && rows == 0) || rows >= kMaxDim)
+    return fail(NVFP4_ERR_SHAPE, "%s: rows must be in [%d, 2^31), got %lld", fn, allow_empty ? 0 : 1, (long long)rows);
+  if (k <= 0 || k >= kMaxDim) return fail(NVFP4_ERR_SHAPE, "%s: K must be in [16, 2^31), got %lld", fn, (long long)k);
+  if (k % NVFP4_BLOCK_SIZE)
+    return fail(NVFP4_ERR_SHAPE, "%s: NVFP4 needs K divisible by %d, got %lld", fn, NVFP4_BLOCK_SIZE, (long long)k);
+  if ((double)rows * (double)k >= 9.0e18) return fail(NVFP4_ERR_SHAPE, "%s: rows*K overflows", fn);
+  return NVFP4_OK;
+}
+
+int check_group(const char* fn, int g, int64_t k, bool allow_none) {
+  if (allow_none && g == 0) return NVFP4_OK;
+  if (g < 2 || g > NVFP4_MAX_ROTATION_GROUP || (g & (g - 1)))
+    return fail(NVFP4_ERR_ARG, "%s: rotation group must be a power of two in [2, %d]%s, got %d", fn,
+                NVFP4_MAX_ROTATION_GROUP, allow_none ? " or 0" : "", g);
+  if (k % g) return fail(NVFP4_ERR_ARG, "%s: rotation group %d does not divide K %lld", fn, g, (long long)k);
+  return NVFP4_OK;
+}
+
+float inv_sqrt(int g) { return g > 1 ? (float)(1.0 / sqrt((double)g)) : 1.0f; }
+
+struct LinearWorkspace {
+  uint8_t* codes;
+  uint8_t* scales;
+  float* partials;
+  float* gsf;
+  size_t bytes;
+};
+
+LinearWorkspace carve(void* base, int64_t m, int64_t k) {
+  // offsets first, pointers only for a real base
+  const size_t o_codes = 0;
+  const size_t o_scales = align_up(o_codes + (size_t)m * (size_t)(k / 2));
+  const size_t o_partials = align_up(o_scales + nvfp4_scale_bytes(m, k));
+  const size_t o_gsf = align_up(o_partials + sizeof(float) * nvfp4::kMaxAmaxPartials);
+  LinearWorkspace w{nullptr, nullptr, nullptr, nullptr, align_up(o_gsf + sizeof(float))};
+  if (base != nullptr) {
+    uint8_t* p = static_cast<uint8_t*>(base);
+    w.codes = p + o_codes;
+    w.scales = p + o_scales;
+    w.partials = reinterpret_cast<float*>(p + o_partials);
+    w.gsf = reinterpret_cast<float*>(p + o_gsf);
+  }
+  return w;
+}
+
+int quantize_impl(const char* fn, const void* x, int64_t m, int64_t k, const float* gsf_static, int group,
+                  uint8_t* codes, uint8_t* scales, float* gsf_out, float* partials, hipStream_t s) {
+  int n_partials = 0;
+  const float c = inv_sqrt(group);
+  if (gsf_static == nullptr) {
+    int rc = hip_status(nvfp4::launch_amax_partials(static_cast<const uint16_t*>(x), m, k, group, c, partials,
+                                                    &n_partials, s), fn);
+    if (rc) return rc;
+  }
+  return hip_status(nvfp4::launch_quantize(static_cast<const uint16_t*>(x), m, k, group, c, gsf_static, partials,
+                                           n_partials, codes, scales, gsf_out, s), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t nvfp4_scale_bytes(int64_t rows, int64_t k) {
+  if (rows <= 0 || k <= 0) return 0;
+  const int64_t kt = (k + NVFP4_SCALE_TILE_K - 1) / NVFP4_SCALE_TILE_K;
+  return (size_t)kt * (size_t)rows * 8u;
+}
+
+size_t nvfp4_quantize_workspace_bytes(void) { return align_up(sizeof(float) * nvfp4::kMaxAmaxPartials); }
+
+size_t nvfp4_linear_workspace_bytes(int64_t m, int64_t k) {
+  if (m < 0 || k <= 0) return 0;
+  return carve(nullptr, m, k).bytes;
+}
+
+const char* nvfp4_last_error(void) { return g_err; }
+
+int rotate_activation(const void* x, int x_dtype, void* y, int y_dtype, int64_t rows, int64_t k, int group_size,
+                      void* stream) {
+  const char* fn = "rotate_activation";
+  g_err[0] = 0;
+  if (int rc = check_rows_k(fn, rows, k, true)) return rc;
+  if (int rc = check_group(fn, group_size, k, false)) return rc;
+  if ((x_dtype != NVFP4_DTYPE_BF16 && x_dtype != NVFP4_DTYPE_F32) ||
+      (y_dtype != NVFP4_DTYPE_BF16 && y_dtype != NVFP4_DTYPE_F32))
+    return fail(NVFP4_ERR_ARG, "%s: dtype must be NVFP4_DTYPE_BF16 or NVFP4_DTYPE_F32", fn);
+  if (rows == 0) return NVFP4_OK;
+  if (x == nullptr || y == nullptr) return fail(NVFP4_ERR_ARG, "%s: x and y must not be NULL", fn);
+  if (x == y && x_dtype != y_dtype) return fail(NVFP4_ERR_ARG, "%s: in-place rotation needs equal dtypes", fn);
+  return hip_status(nvfp4::launch_rotate(x, x_dtype == NVFP4_DTYPE_BF16, y, y_dtype == NVFP4_DTYPE_BF16, rows, k,
+                                         group_size, inv_sqrt(group_size), static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int nvfp4_quantize_weight(const void* w, int64_t n, int64_t k, uint8_t* packed, uint8_t* inv_scale,
+                          float* global_sf_w, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "nvfp4_quantize_weight";
+  g_err[0] = 0;
+  if (int rc = check_rows_k(fn, n, k, false)) return rc;
+  if (!w || !packed || !inv_scale || !global_sf_w) return fail(NVFP4_ERR_ARG, "%s: NULL tensor argument", fn);
+  if (!workspace || workspace_bytes < nvfp4_quantize_workspace_bytes() ||
+      ((uintptr_t)workspace % NVFP4_WORKSPACE_ALIGN))
+    return fail(NVFP4_ERR_WORKSPACE, "%s: need a %d-byte aligned workspace of %zu bytes, got %zu", fn,
+                NVFP4_WORKSPACE_ALIGN, nvfp4_quantize_workspace_bytes(), workspace_bytes);
+  return quantize_impl(fn, w, n, k, nullptr, 0, packed, inv_scale, global_sf_w, static_cast<float*>(workspace),
+                       static_cast<hipStream_t>(stream));
+}
+
+int nvfp4_quantize_activation(const void* x, int64_t m, int64_t k, const float* global_sf_x, int rotation_group,
+                              uint8_t* codes, uint8_t* scales, float* gsf_out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  const char* fn = "nvfp4_quantize_activation";
+  g_err[0] = 0;
+  if (int rc = check_rows_k(fn, m, k, true)) return rc;
+  if (int rc = check_group(fn, rotation_group, k, true)) return rc;
+  if (m == 0) return NVFP4_OK;
+  if (!x || !codes || !scales) return fail(NVFP4_ERR_ARG, "%s: NULL tensor argument", fn);
+  if (global_sf_x == nullptr &&
+      (!workspace || workspace_bytes < nvfp4_quantize_workspace_bytes() ||
+       ((uintptr_t)workspace % NVFP4_WORKSPACE_ALIGN)))
+    return fail(NVFP4_ERR_WORKSPACE, "%s: the dynamic scale needs a %d-byte aligned workspace of %zu bytes", fn,
+                NVFP4_WORKSPACE_ALIGN, nvfp4_quantize_workspace_bytes());
+  return quantize_impl(fn, x, m, k, global_sf_x, rotation_group, codes, scales, gsf_out,
+                       static_cast<float*>(workspace), static_cast<hipStream_t>(stream));
+}
+
+int nvfp4_gemm(const uint8_t* x_codes, const uint8_t* x_scale, int64_t m, int64_t k, const uint8_t* packed,
+               const uint8_t* inv_scale, int64_t n, const float* gsf_x, const float* gsf_w, const void* bias,
+               void* out, void* stream) {
+  const char* fn = "nvfp4_gemm";
+  g_err[0] = 0;
+  if (int rc = check_rows_k(fn, m, k, true)) return rc;
+  if (n <= 0 || n >= kMaxDim) return fail(NVFP4_ERR_SHAPE, "%s: out_features must be in [1, 2^31), got %lld", fn, (long long)n);
+  if (m == 0) return NVFP4_OK;
+  if (!x_codes || !x_scale || !packed || !inv_scale || !gsf_x || !gsf_w || !out)
+    return fail(NVFP4_ERR_ARG, "%s: NULL tensor argument", fn);
+  return hip_status(nvfp4::launch_gemm(x_codes, x_scale, m, k, packed, inv_scale, n, gsf_x, gsf_w,
+                                       static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(out),
+                                       static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int nvfp4_linear(const void* x, int64_t m, int64_t k, const uint8_t* packed, const uint8_t* inv_scale,
+                 const float* global_sf_w, const void* bias, int64_t out_features, const float* global_sf_x,
+                 int rotation_group, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "nvfp4_linear";
+  g_err[0] = 0;
+  if (int rc = check_rows_k(fn, m, k, true)) return rc;
+  if (int rc = check_group(fn, rotation_group, k, true)) return rc;
+  if (out_features <= 0 || out_features >= kMaxDim)
+    return fail(NVFP4_ERR_SHAPE, "%s: out_features must be in [1, 2^31), got %lld", fn, (long long)out_features);
+  if (m == 0) return NVFP4_OK;
+  if (!x || !packed || !inv_scale || !global_sf_w || !out) return fail(NVFP4_ERR_ARG, "%s: NULL tensor argument", fn);
+  const size_t need = nvfp4_linear_workspace_bytes(m, k);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % NVFP4_WORKSPACE_ALIGN))
+    return fail(NVFP4_ERR_WORKSPACE, "%s: need a %d-byte aligned workspace of %zu bytes, got %zu", fn,
+                NVFP4_WORKSPACE_ALIGN, need, workspace_bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const LinearWorkspace ws = carve(workspace, m, k);
+  if (int rc = quantize_impl(fn, x, m, k, global_sf_x, rotation_group, ws.codes, ws.scales, ws.gsf, ws.partials, s))
+    return rc;
+  return hip_status(nvfp4::launch_gemm(ws.codes, ws.scales, m, k, packed, inv_scale, out_features, ws.gsf,
+                                       global_sf_w, static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(out), s),
+                    fn);
+}
+
+int nvfp4_scale_to_canonical(const uint8_t* layout, uint8_t* canonical, int64_t rows, int64_t k, void* stream) {
+  const char* fn = "nvfp4_scale_to_canonical";
+  g_err[0] = 0;
+  if (int rc = check_rows_k(fn, rows, k, true)) return rc;
+  if (rows == 0) return NVFP4_OK;
+  if (!layout || !canonical) return fail(NVFP4_ERR_ARG, "%s: NULL tensor argument", fn);
+  return hip_status(nvfp4::launch_scale_layout(layout, canonical, rows, k, true, static_cast<hipStream_t>(stream)), fn);
+}
+
+int nvfp4_scale_from_canonical(const uint8_t* canonical, uint8_t* layout, int64_t rows, int64_t k, void* stream) {
+  const char* fn = "nvfp4_scale_from_canonical";
+  g_err[0] = 0;
+  if (int rc = check_rows_k(fn, rows, k, true)) return rc;
+  if (rows == 0) return NVFP4_OK;
+  if (!layout || !canonical) return fail(NVFP4_ERR_ARG, "%s: NULL tensor argument", fn);
+  return hip_status(nvfp4::launch_scale_layout(canonical, layout, rows, k, false, static_cast<hipStream_t>(stream)), fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,266 @@
+// Activation / weight side of the NVFP4 linear on gfx950: abs-max reduction for the
+// dynamic global scale, the fused (rotate +) quantize pass, the stand-alone block
+// Hadamard rotation, and the scale-layout conversions.
+//
+// What is computed: "minimax_h3_nvfp4_decoder" page, nvfp4_linear_inference (a
+// dynamic global scale from the call's 2-D input, then the FP4 quantize) and
+// NVFP4DecoderLinear.forward / rotate_activation (the block rotation applied to the
+// activation before it).  All of it is HBM-bound streaming: every kernel reads its
+// input once with 16-byte loads; a 16-value block (32 bytes of bf16) is one lane's
+// unit of work, so the per-block max and the per-block scale never leave registers.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nvfp4_device.h"
+#include "nvfp4_launch.h"
+
+namespace nvfp4 {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+struct Chunk16 {
+  float v[16];
+};
+
+__device__ __forceinline__ void load16_bf16(const uint16_t* __restrict__ p, float (&v)[16]) {
+  const uint4 a = reinterpret_cast<const uint4*>(p)[0];
+  const uint4 b = reinterpret_cast<const uint4*>(p)[1];
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+__device__ __forceinline__ void load16_f32(const float* __restrict__ p, float (&v)[16]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 t = reinterpret_cast<const float4*>(p)[i];
+    v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+  }
+}
+
+// Block-wide max of a non-negative value; every thread gets the result.
+__device__ __forceinline__ float block_max(float x, float* lds) {
+  x = wave_max(x);
+  const int wid = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) lds[wid] = x;
+  __syncthreads();
+  float r = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kThreads / 64; ++i) r = fmaxf(r, lds[i]);
+  __syncthreads();
+  return r;
+}
+
+// Pass 1 of the dynamic scale: every block writes the max |v| of its share of the
+// (optionally rotated, bf16-rounded) input to partials[blockIdx.x].  Lanes take
+// consecutive 16-value chunks, so the lanes holding one rotation group are
+// consecutive and aligned (the group divides the row length).
+template <bool kRotate>
+__global__ void __launch_bounds__(kThreads) amax_partial_kernel(const uint16_t* __restrict__ x, int64_t n_chunks,
+                                                                 int group, float inv_sqrt_g,
+                                                                 float* __restrict__ partials) {
+  __shared__ float lds[kThreads / 64];
+  float m = 0.0f;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t c0 = (int64_t)blockIdx.x * kThreads; c0 < n_chunks; c0 += stride) {
+    const int64_t c = c0 + threadIdx.x;
+    float v[16];
+    if (c < n_chunks) {
+      load16_bf16(x + c * 16, v);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = 0.0f;
+    }
+    if (kRotate) rotate16_bf16(v, group, inv_sqrt_g);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+  }
+  m = block_max(m, lds);
+  if (threadIdx.x == 0) partials[blockIdx.x] = m;
+}
+
+// Pass 2: quantize.  Eight consecutive lanes own one 128-wide K tile of one row
+// (lane j of the eight owns the 16-block j of the tile), so each group of eight
+// reads 256 contiguous bytes, writes 64 contiguous code bytes and the 8 scale bytes
+// that are contiguous in the k-tile-major scale layout.
+template <bool kRotate>
+__global__ void __launch_bounds__(kThreads) quantize_kernel(
+    const uint16_t* __restrict__ x, int64_t m_rows, int64_t k, int group, float inv_sqrt_g,
+    const float* __restrict__ static_gsf, const float* __restrict__ partials, int n_partials,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gsf_out) {
+  __shared__ float lds[kThreads / 64];
+  float gsf;
+  if (static_gsf != nullptr) {
+    gsf = *static_gsf;
+  } else {
+    float a = 0.0f;
+    for (int i = threadIdx.x; i < n_partials; i += kThreads) a = fmaxf(a, partials[i]);
+    a = block_max(a, lds);
+    gsf = global_scale_from_amax(a);
+  }
+  if (gsf_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *gsf_out = gsf;
+
+  const int64_t kt_count = (k + kScaleTileK - 1) / kScaleTileK;
+  const int64_t nb = k / kBlock;
+  const int64_t unit = (int64_t)blockIdx.x * (kThreads / 8) + (threadIdx.x >> 3);
+  const int j = threadIdx.x & 7;
+  const int64_t row = unit / kt_count;
+  const int64_t kt = unit - row * kt_count;
+  const int64_t blk = kt * 8 + j;
+  const bool in_row = row < m_rows;
+  const bool valid = in_row && blk < nb;
+
+  float v[16];
+  if (valid) {
+    load16_bf16(x + row * k + blk * kBlock, v);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = 0.0f;
+  }
+  if (kRotate) rotate16_bf16(v, group, inv_sqrt_g);
+
+  float bmax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) bmax = fmaxf(bmax, fabsf(v[i]));
+  const uint32_t s8 = block_scale_byte(gsf, bmax);
+  uint32_t w0 = 0, w1 = 0;
+  if (s8 != 0) {
+    const float r = __fdiv_rn(gsf, e4m3_decode(s8));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w0 |= e2m1_encode(__fmul_rn(v[i], r)) << (4 * i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w1 |= e2m1_encode(__fmul_rn(v[8 + i], r)) << (4 * i);
+  }
+  if (valid) {
+    *reinterpret_cast<uint2*>(codes + row * (k / 2) + blk * 8) = make_uint2(w0, w1);
+  }
+  if (in_row && kt < kt_count) {
+    scales[(kt * m_rows + row) * 8 + j] = valid ? (uint8_t)s8 : (uint8_t)0;
+  }
+}
+
+// Stand-alone rotation: x (bf16 or fp32) -> y (bf16 or fp32), one 16-value chunk per lane.
+template <typename Tin, bool kOutBf16>
+__global__ void __launch_bounds__(kThreads) rotate_kernel(const Tin* __restrict__ x, void* __restrict__ y,
+                                                          int64_t n_chunks, int group, float inv_sqrt_g) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t c0 = (int64_t)blockIdx.x * kThreads; c0 < n_chunks; c0 += stride) {
+    const int64_t c = c0 + threadIdx.x;
+    float v[16];
+    if (c < n_chunks) {
+      if constexpr (sizeof(Tin) == 2) load16_bf16(reinterpret_cast<const uint16_t*>(x) + c * 16, v);
+      else load16_f32(reinterpret_cast<const float*>(x) + c * 16, v);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = 0.0f;
+    }
+    fwht16_local(v, group);
+    fwht16_cross(v, group);
+    if (c < n_chunks) {
+      if constexpr (kOutBf16) {
+        uint32_t w[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          w[i] = f32_to_bf16(__fmul_rn(v[2 * i], inv_sqrt_g)) | (f32_to_bf16(__fmul_rn(v[2 * i + 1], inv_sqrt_g)) << 16);
+        uint4* out = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(y) + c * 16);
+        out[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        out[1] = make_uint4(w[4], w[5], w[6], w[7]);
+      } else {
+        float4* out = reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + c * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          out[i] = make_float4(__fmul_rn(v[4 * i], inv_sqrt_g), __fmul_rn(v[4 * i + 1], inv_sqrt_g),
+                               __fmul_rn(v[4 * i + 2], inv_sqrt_g), __fmul_rn(v[4 * i + 3], inv_sqrt_g));
+      }
+    }
+  }
+}
+
+// Scale-layout conversion; one thread per (row, 128-K tile): 8 bytes.
+template <bool kToCanonical>
+__global__ void __launch_bounds__(kThreads) scale_layout_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                                int64_t rows, int64_t k) {
+  const int64_t kt_count = (k + kScaleTileK - 1) / kScaleTileK;
+  const int64_t nb = k / kBlock;
+  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (t >= rows * kt_count) return;
+  const int64_t kt = t / rows;
+  const int64_t row = t - kt * rows;
+  for (int j = 0; j < 8; ++j) {
+    const int64_t b = kt * 8 + j;
+    const int64_t lay = (kt * rows + row) * 8 + j;
+    if (kToCanonical) {
+      if (b < nb) dst[row * nb + b] = src[lay];
+    } else {
+      dst[lay] = b < nb ? src[row * nb + b] : (uint8_t)0;
+    }
+  }
+}
+
+int64_t grid_for(int64_t n_chunks, int64_t cap) {
+  int64_t g = (n_chunks + kThreads - 1) / kThreads;
+  if (g > cap) g = cap;
+  return g < 1 ? 1 : g;
+}
+
+}  // namespace
+
+hipError_t launch_amax_partials(const uint16_t* x, int64_t rows, int64_t k, int group, float inv_sqrt_g,
+                                float* partials, int* n_partials, hipStream_t s) {
+  const int64_t n_chunks = rows * k / kBlock;
+  const int grid = (int)grid_for(n_chunks, kMaxAmaxPartials);
+  *n_partials = grid;
+  if (group > 1)
+    hipLaunchKernelGGL(amax_partial_kernel<true>, dim3(grid), dim3(kThreads), 0, s, x, n_chunks, group, inv_sqrt_g, partials);
+  else
+    hipLaunchKernelGGL(amax_partial_kernel<false>, dim3(grid), dim3(kThreads), 0, s, x, n_chunks, group, inv_sqrt_g, partials);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t k, int group, float inv_sqrt_g,
+                           const float* static_gsf, const float* partials, int n_partials,
+                           uint8_t* codes, uint8_t* scales, float* gsf_out, hipStream_t s) {
+  const int64_t kt_count = (k + kScaleTileK - 1) / kScaleTileK;
+  const int64_t units = rows * kt_count;
+  const int64_t grid = (units + (kThreads / 8) - 1) / (kThreads / 8);
+  if (group > 1)
+    hipLaunchKernelGGL(quantize_kernel<true>, dim3((uint32_t)grid), dim3(kThreads), 0, s, x, rows, k, group, inv_sqrt_g,
+                       static_gsf, partials, n_partials, codes, scales, gsf_out);
+  else
+    hipLaunchKernelGGL(quantize_kernel<false>, dim3((uint32_t)grid), dim3(kThreads), 0, s, x, rows, k, group, inv_sqrt_g,
+                       static_gsf, partials, n_partials, codes, scales, gsf_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_rotate(const void* x, bool x_bf16, void* y, bool y_bf16, int64_t rows, int64_t k, int group,
+                         float inv_sqrt_g, hipStream_t s) {
+  const int64_t n_chunks = rows * k / kBlock;
+  const int grid = (int)grid_for(n_chunks, 8192);
+  if (x_bf16 && y_bf16)
+    hipLaunchKernelGGL((rotate_kernel<uint16_t, true>), dim3(grid), dim3(kThreads), 0, s, (const uint16_t*)x, y, n_chunks, group, inv_sqrt_g);
+  else if (x_bf16)
+    hipLaunchKernelGGL((rotate_kernel<uint16_t, false>), dim3(grid), dim3(kThreads), 0, s, (const uint16_t*)x, y, n_chunks, group, inv_sqrt_g);
+  else if (y_bf16)
+    hipLaunchKernelGGL((rotate_kernel<float, true>), dim3(grid), dim3(kThreads), 0, s, (const float*)x, y, n_chunks, group, inv_sqrt_g);
+  else
+    hipLaunchKernelGGL((rotate_kernel<float, false>), dim3(grid), dim3(kThreads), 0, s, (const float*)x, y, n_chunks, group, inv_sqrt_g);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale_layout(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t k, bool to_canonical, hipStream_t s) {
+  const int64_t kt_count = (k + kScaleTileK - 1) / kScaleTileK;
+  const int64_t n = rows * kt_count;
+  const int64_t grid = (n + kThreads - 1) / kThreads;
+  if (to_canonical)
+    hipLaunchKernelGGL(scale_layout_kernel<true>, dim3((uint32_t)grid), dim3(kThreads), 0, s, src, dst, rows, k);
+  else
+    hipLaunchKernelGGL(scale_layout_kernel<false>, dim3((uint32_t)grid), dim3(kThreads), 0, s, src, dst, rows, k);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

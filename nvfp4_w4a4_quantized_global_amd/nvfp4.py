@@ -1,0 +1,268 @@
+"""Python binding of libnvfp4.so over torch device tensors.
+
+Argument marshalling only: every arithmetic step runs in the library's gfx950
+kernels.  torch provides device memory and the current stream.  Names follow
+the "minimax_h3_nvfp4_decoder" page: ``rotate_activation``,
+``nvfp4_linear_inference`` (here ``nvfp4_linear``) and ``NVFP4DecoderLinear``
+(here ``NVFP4Linear``), plus the weight quantizer of the conversion script
+("convert_minimax_h3_text_encoder_nvfp4.py", quantize_language_linear).
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import check, lib
+
+NVFP4_BLOCK_SIZE = 16
+SCALE_TILE_K = 128
+MAX_ROTATION_GROUP = 128
+
+
+def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p | None:
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require_cuda(name: str, t: torch.Tensor, dtype: torch.dtype | None = None, dim: int | None = None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dimensions, got shape {list(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.data_ptr() % 16:
+        raise ValueError(f"{name} must be 16-byte aligned")
+
+
+def scale_bytes(rows: int, k: int) -> int:
+    """Size of the block-scale array of a [rows, k] tensor (k-tile-major layout)."""
+    return int(lib().nvfp4_scale_bytes(rows, k))
+
+
+def linear_workspace_bytes(m: int, k: int) -> int:
+    return int(lib().nvfp4_linear_workspace_bytes(m, k))
+
+
+def quantize_workspace_bytes() -> int:
+    return int(lib().nvfp4_quantize_workspace_bytes())
+
+
+def _scalar_f32(v, device) -> torch.Tensor:
+    if isinstance(v, torch.Tensor):
+        _require_cuda("global scale", v, torch.float32)
+        if v.numel() != 1:
+            raise ValueError("a global scale must hold one value")
+        return v
+    return torch.tensor(float(v), dtype=torch.float32, device=device)
+
+
+def rotate_activation(x: torch.Tensor, group_size: int, out_dtype: torch.dtype | None = None) -> torch.Tensor:
+    """Block Hadamard rotation of the last dimension, groups of ``group_size``.
+
+    bf16 -> bf16 on the activation path; fp32 -> fp32 or fp32 -> bf16 for the
+    offline weight fold.
+    """
+    _require_cuda("x", x)
+    out_dtype = out_dtype or x.dtype
+    codes = {torch.bfloat16: _lib.NVFP4_DTYPE_BF16, torch.float32: _lib.NVFP4_DTYPE_F32}
+    if x.dtype not in codes or out_dtype not in codes:
+        raise ValueError(f"rotate_activation supports bf16/fp32, got {x.dtype} -> {out_dtype}")
+    k = x.shape[-1]
+    rows = x.numel() // k if k else 0
+    y = torch.empty(x.shape, dtype=out_dtype, device=x.device)
+    check(lib().rotate_activation(_ptr(x), codes[x.dtype], _ptr(y), codes[out_dtype], rows, k, int(group_size),
+                                  _stream(x.device)))
+    return y
+
+
+def quantize_weight(w: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """bf16 weight [N, K] -> (packed uint8 [N, K/2], block scales uint8 (layout), global scale fp32 0-d)."""
+    _require_cuda("weight", w, torch.bfloat16, 2)
+    n, k = w.shape
+    packed = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((scale_bytes(n, k),), dtype=torch.uint8, device=w.device)
+    gsf = torch.empty((), dtype=torch.float32, device=w.device)
+    ws = torch.empty((quantize_workspace_bytes(),), dtype=torch.uint8, device=w.device)
+    check(lib().nvfp4_quantize_weight(_ptr(w), n, k, _ptr(packed), _ptr(scales), _ptr(gsf), _ptr(ws), ws.numel(),
+                                      _stream(w.device)))
+    return packed, scales, gsf
+
+
+def quantize_activation(x: torch.Tensor, global_sf_x=None, rotation_group: int = 0
+                        ) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """bf16 [M, K] -> (codes uint8 [M, K/2], scales uint8 (layout), the global scale used, fp32 0-d)."""
+    _require_cuda("x", x, torch.bfloat16, 2)
+    m, k = x.shape
+    codes = torch.empty((m, k // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((max(scale_bytes(m, k), 1),), dtype=torch.uint8, device=x.device)
+    gsf = torch.empty((), dtype=torch.float32, device=x.device)
+    g = None if global_sf_x is None else _scalar_f32(global_sf_x, x.device)
+    ws = torch.empty((quantize_workspace_bytes(),), dtype=torch.uint8, device=x.device)
+    check(lib().nvfp4_quantize_activation(_ptr(x), m, k, _ptr(g), int(rotation_group), _ptr(codes), _ptr(scales),
+                                          _ptr(gsf), _ptr(ws), ws.numel(), _stream(x.device)))
+    return codes, scales[: scale_bytes(m, k)], gsf
+
+
+def nvfp4_gemm(x_codes: torch.Tensor, x_scales: torch.Tensor, packed: torch.Tensor, inv_scale: torch.Tensor,
+               global_sf_x, global_sf_w, bias: torch.Tensor | None = None, out: torch.Tensor | None = None
+               ) -> torch.Tensor:
+    """Block-scaled GEMM on already quantized activations; bf16 [M, N]."""
+    _require_cuda("x_codes", x_codes, torch.uint8, 2)
+    _require_cuda("packed", packed, torch.uint8, 2)
+    m, half_k = x_codes.shape
+    n = packed.shape[0]
+    k = 2 * half_k
+    if packed.shape[1] != half_k:
+        raise ValueError(f"packed NVFP4 weight must be uint8 [{n}, {half_k}], got {list(packed.shape)}")
+    _require_cuda("x_scales", x_scales, torch.uint8)
+    _require_cuda("inv_scale", inv_scale, torch.uint8)
+    if x_scales.numel() < scale_bytes(m, k) or inv_scale.numel() < scale_bytes(n, k):
+        raise ValueError("scale arrays are smaller than nvfp4_scale_bytes")
+    gx = _scalar_f32(global_sf_x, x_codes.device)
+    gw = _scalar_f32(global_sf_w, x_codes.device)
+    if bias is not None:
+        _require_cuda("bias", bias, torch.bfloat16)
+        if bias.numel() != n:
+            raise ValueError(f"bias must have {n} elements, got {bias.numel()}")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=x_codes.device)
+    check(lib().nvfp4_gemm(_ptr(x_codes), _ptr(x_scales), m, k, _ptr(packed), _ptr(inv_scale), n, _ptr(gx), _ptr(gw),
+                           _ptr(bias), _ptr(out), _stream(x_codes.device)))
+    return out
+
+
+def nvfp4_linear(x: torch.Tensor, packed: torch.Tensor, inv_scale: torch.Tensor, global_sf_w: torch.Tensor,
+                 bias: torch.Tensor | None, out_features: int, global_sf_x=None, rotation_group: int = 0,
+                 workspace: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """The NVFP4 W4A4 linear: (rotate,) global scale, quantize, block-scaled GEMM, alpha, bias.
+
+    ``global_sf_x=None`` computes the activation scale dynamically from the
+    call's 2-D input.  Leading dimensions of x are flattened and restored.
+    """
+    if x.dtype != torch.bfloat16:
+        raise ValueError(f"x must be bf16, got {x.dtype}")
+    orig = x.shape
+    k = orig[-1]
+    x2d = x.reshape(-1, k)
+    if not x2d.is_contiguous():
+        x2d = x2d.contiguous()
+    _require_cuda("x", x2d, torch.bfloat16, 2)
+    _require_cuda("packed", packed, torch.uint8, 2)
+    if packed.shape[0] != out_features or packed.shape[1] * 2 != k:
+        raise ValueError(f"packed NVFP4 weight must be uint8 [{out_features}, {k // 2}], got "
+                         f"{packed.dtype} {list(packed.shape)}")
+    _require_cuda("inv_scale", inv_scale, torch.uint8)
+    if inv_scale.numel() < scale_bytes(out_features, k):
+        raise ValueError("inv_scale is smaller than nvfp4_scale_bytes(out_features, K)")
+    gw = _scalar_f32(global_sf_w, x.device)
+    gx = None if global_sf_x is None else _scalar_f32(global_sf_x, x.device)
+    if bias is not None:
+        _require_cuda("bias", bias, torch.bfloat16)
+        if bias.numel() != out_features:
+            raise ValueError(f"bias must have {out_features} elements, got {bias.numel()}")
+    m = x2d.shape[0]
+    need = linear_workspace_bytes(m, k)
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((m, out_features), dtype=torch.bfloat16, device=x.device)
+    check(lib().nvfp4_linear(_ptr(x2d), m, k, _ptr(packed), _ptr(inv_scale), _ptr(gw), _ptr(bias), out_features,
+                             _ptr(gx), int(rotation_group), _ptr(out), _ptr(workspace), workspace.numel(),
+                             _stream(x.device)))
+    return out.reshape(*orig[:-1], out_features)
+
+
+def scale_to_canonical(layout: torch.Tensor, rows: int, k: int) -> torch.Tensor:
+    """Block scales from the library layout to row-major uint8 [rows, K/16]."""
+    _require_cuda("layout", layout, torch.uint8)
+    out = torch.empty((rows, k // NVFP4_BLOCK_SIZE), dtype=torch.uint8, device=layout.device)
+    check(lib().nvfp4_scale_to_canonical(_ptr(layout), _ptr(out), rows, k, _stream(layout.device)))
+    return out
+
+
+def scale_from_canonical(canonical: torch.Tensor) -> torch.Tensor:
+    """Row-major uint8 [rows, K/16] block scales to the library layout."""
+    _require_cuda("canonical", canonical, torch.uint8, 2)
+    rows, nb = canonical.shape
+    k = nb * NVFP4_BLOCK_SIZE
+    out = torch.empty((max(scale_bytes(rows, k), 1),), dtype=torch.uint8, device=canonical.device)
+    check(lib().nvfp4_scale_from_canonical(_ptr(canonical), _ptr(out), rows, k, _stream(canonical.device)))
+    return out[: scale_bytes(rows, k)]
+
+
+class NVFP4Linear:
+    """Inference-only NVFP4 W4A4 linear holding a packed weight.
+
+    Mirrors NVFP4DecoderLinear's frozen inference path: ``from_linear`` folds
+    the optional block rotation into the weight in fp32, rounds it to bf16 and
+    quantizes it once; ``__call__`` runs :func:`nvfp4_linear` with a dynamic
+    (``act_scale='dynamic'``), static (``'static'``, 2688 / input_amax) or unit
+    (``'unit'``) activation scale.
+    """
+
+    ACT_SCALES = ("dynamic", "static", "unit")
+
+    def __init__(self, packed, inv_scale, global_sf_w, bias, in_features, rotation_group=None,
+                 act_scale="dynamic", input_amax=None):
+        if in_features % NVFP4_BLOCK_SIZE:
+            raise ValueError(f"NVFP4 needs in_features divisible by {NVFP4_BLOCK_SIZE}, got {in_features}")
+        if rotation_group is not None and in_features % rotation_group:
+            raise ValueError(f"rotation group {rotation_group} does not divide in_features {in_features}")
+        if act_scale not in self.ACT_SCALES:
+            raise ValueError(f"act_scale must be one of {self.ACT_SCALES}, got {act_scale!r}")
+        if packed.dtype != torch.uint8 or packed.shape[1] * 2 != in_features:
+            raise ValueError(f"packed NVFP4 weight must be uint8 [{packed.shape[0]}, {in_features // 2}], "
+                             f"got {packed.dtype} {list(packed.shape)}")
+        self.packed, self.inv_scale, self.global_sf_w = packed, inv_scale, global_sf_w
+        self.bias = bias
+        self.in_features = in_features
+        self.out_features = packed.shape[0]
+        self.rotation_group = rotation_group
+        self.act_scale = act_scale
+        self.input_amax = input_amax
+        self._gsf_x = None
+
+    @classmethod
+    def from_weight(cls, weight: torch.Tensor, bias: torch.Tensor | None = None, rotation_group: int | None = None,
+                    act_scale: str = "dynamic", input_amax=None) -> "NVFP4Linear":
+        """weight: [out, in] on the GPU (any float dtype; the fold runs in fp32)."""
+        out_f, in_f = weight.shape
+        if in_f % NVFP4_BLOCK_SIZE:
+            raise ValueError(f"NVFP4 needs in_features divisible by {NVFP4_BLOCK_SIZE}, got {in_f}")
+        if rotation_group is not None:
+            if in_f % rotation_group:
+                raise ValueError(f"rotation group {rotation_group} does not divide in_features {in_f}")
+            w = rotate_activation(weight.float().contiguous(), rotation_group, out_dtype=torch.bfloat16)
+        else:
+            w = weight.to(torch.bfloat16).contiguous()
+        packed, inv_scale, gsf_w = quantize_weight(w)
+        b = None if bias is None else bias.to(torch.bfloat16).contiguous()
+        return cls(packed, inv_scale, gsf_w, b, in_f, rotation_group, act_scale, input_amax)
+
+    def activation_global_sf(self):
+        if self.act_scale == "dynamic":
+            return None
+        if self._gsf_x is None:
+            if self.act_scale == "unit":
+                self._gsf_x = torch.ones((), dtype=torch.float32, device=self.packed.device)
+            else:
+                if self.input_amax is None:
+                    raise ValueError("act_scale='static' needs input_amax")
+                amax = torch.as_tensor(self.input_amax, dtype=torch.float32, device=self.packed.device)
+                # 2688 / amax.clamp(min=1e-12) in fp32; computed once on the device by torch
+                self._gsf_x = torch.tensor(2688.0, dtype=torch.float32, device=amax.device) / amax.clamp(min=1e-12)
+        return self._gsf_x
+
+    def __call__(self, x: torch.Tensor) -> torch.Tensor:
+        return nvfp4_linear(x.to(torch.bfloat16), self.packed, self.inv_scale, self.global_sf_w, self.bias,
+                            self.out_features, self.activation_global_sf(), self.rotation_group or 0)

@@ -1,0 +1,95 @@
+"""Host-side checks of the C ABI: the library loads, exports every function the
+header declares, and rejects bad arguments before touching the GPU.  These run
+without a GPU: every call here fails validation, so nothing is launched."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+from nvfp4_w4a4_quantized_global_amd import _lib
+from nvfp4_w4a4_quantized_global_amd._lib import (NVFP4_ERR_ARG, NVFP4_ERR_SHAPE, NVFP4_ERR_WORKSPACE,
+                                                   header_functions, lib)
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libnvfp4.so not built")
+
+
+def test_header_declares_the_boundary():
+    names = header_functions()
+    for required in ("nvfp4_quantize_weight", "rotate_activation", "nvfp4_linear", "nvfp4_gemm",
+                     "nvfp4_quantize_activation", "nvfp4_scale_bytes", "nvfp4_linear_workspace_bytes",
+                     "nvfp4_scale_to_canonical", "nvfp4_scale_from_canonical", "nvfp4_last_error"):
+        assert required in names
+    assert set(names) == set(_lib.SIGNATURES), set(names) ^ set(_lib.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    handle = lib()
+    for name in header_functions():
+        assert hasattr(handle, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(header_functions()) <= exported
+
+
+def test_sizes():
+    L = lib()
+    assert L.nvfp4_scale_bytes(4096, 5120) == 40 * 4096 * 8
+    assert L.nvfp4_scale_bytes(3, 208) == 2 * 3 * 8           # K % 128 != 0: padded tile
+    assert L.nvfp4_scale_bytes(0, 256) == 0
+    assert L.nvfp4_quantize_workspace_bytes() % 256 == 0 and L.nvfp4_quantize_workspace_bytes() >= 4096
+    ws = L.nvfp4_linear_workspace_bytes(4096, 5120)
+    assert ws >= 4096 * 2560 + 40 * 4096 * 8 + 4096 + 4 and ws % 256 == 0
+
+
+def _msg():
+    return lib().nvfp4_last_error().decode()
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("k", [8, 24, 250, 0, -16])
+def test_k_not_multiple_of_block(k):
+    rc = lib().nvfp4_linear(FAKE, 4, k, FAKE, FAKE, FAKE, None, 8, None, 0, FAKE, FAKE, 1 << 20, None)
+    assert rc == NVFP4_ERR_SHAPE
+    assert "K" in _msg()
+
+
+@pytest.mark.parametrize("g", [3, 6, 256, 1, -2, 48])
+def test_bad_rotation_group(g):
+    rc = lib().nvfp4_linear(FAKE, 4, 96, FAKE, FAKE, FAKE, None, 8, None, g, FAKE, FAKE, 1 << 20, None)
+    assert rc in (NVFP4_ERR_ARG,)
+    assert "rotation group" in _msg()
+
+
+def test_rotation_group_must_divide_k():
+    rc = lib().rotate_activation(FAKE, 0, FAKE, 0, 2, 48, 32, None)
+    assert rc == NVFP4_ERR_ARG and "does not divide" in _msg()
+
+
+def test_out_features_and_workspace():
+    assert lib().nvfp4_linear(FAKE, 4, 64, FAKE, FAKE, FAKE, None, 0, None, 0, FAKE, FAKE, 1 << 20, None) == NVFP4_ERR_SHAPE
+    need = lib().nvfp4_linear_workspace_bytes(4, 64)
+    rc = lib().nvfp4_linear(FAKE, 4, 64, FAKE, FAKE, FAKE, None, 8, None, 0, FAKE, FAKE, need - 1, None)
+    assert rc == NVFP4_ERR_WORKSPACE
+    rc = lib().nvfp4_linear(FAKE, 4, 64, FAKE, FAKE, FAKE, None, 8, None, 0, FAKE, ctypes.c_void_p(0x1010), need, None)
+    assert rc == NVFP4_ERR_WORKSPACE   # misaligned
+
+
+def test_null_arguments():
+    assert lib().nvfp4_linear(None, 4, 64, FAKE, FAKE, FAKE, None, 8, None, 0, FAKE, FAKE, 1 << 20, None) == NVFP4_ERR_ARG
+    assert lib().nvfp4_quantize_weight(FAKE, 4, 64, None, FAKE, FAKE, FAKE, 4096, None) == NVFP4_ERR_ARG
+    assert lib().rotate_activation(FAKE, 5, FAKE, 0, 2, 64, 16, None) == NVFP4_ERR_ARG
+
+
+def test_empty_input_is_a_no_op():
+    assert lib().nvfp4_linear(None, 0, 64, None, None, None, None, 8, None, 0, None, None, 0, None) == 0
+    assert lib().nvfp4_quantize_activation(None, 0, 64, None, 0, None, None, None, None, 0, None) == 0
+
+
+def test_binding_raises_value_error():
+    from nvfp4_w4a4_quantized_global_amd._lib import check
+    lib().nvfp4_linear(FAKE, 4, 24, FAKE, FAKE, FAKE, None, 8, None, 0, FAKE, FAKE, 1 << 20, None)
+    with pytest.raises(ValueError, match="divisible by 16"):
+        check(NVFP4_ERR_SHAPE)

@@ -1,0 +1,153 @@
+"""GPU parity of the amax / global-scale, rotation and quantize kernels against the
+CPU oracle: every code byte, scale byte and global scale must be identical."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as o
+import workloads
+from tests._util import layout_padding, layout_to_canonical, oracle_quantize
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def nv():
+    import nvfp4_w4a4_quantized_global_amd as m
+    return m
+
+
+def gpu_quantize(x_cpu: torch.Tensor, gsf=None, g: int = 0):
+    x = x_cpu.to(DEV)
+    m, k = x.shape
+    codes, scales, used = nv().quantize_activation(x, gsf, g)
+    torch.cuda.synchronize()
+    lay = scales.cpu().numpy()
+    assert not layout_padding(lay, m, k).any(), "scale padding bytes must be zero"
+    return codes.cpu().numpy(), layout_to_canonical(lay, m, k), np.float32(used.item())
+
+
+def oracle_expected(x_cpu: torch.Tensor, gsf=None, g: int = 0):
+    xf = x_cpu.float().numpy()
+    if g:
+        xf = o.rotate_activation(xf, g)
+    gs = o.global_sf(o.amax(xf)) if gsf is None else np.float32(gsf)
+    packed, s8 = oracle_quantize(xf, gs)
+    return packed, s8, gs
+
+
+def assert_same(got, exp, what):
+    gc, gs, gg = got
+    ec, es, eg = exp
+    assert gg.view(np.uint32) == np.float32(eg).view(np.uint32), f"{what}: global scale {gg!r} != {eg!r}"
+    assert np.array_equal(gs, es), f"{what}: {int((gs != es).sum())} scale bytes differ"
+    assert np.array_equal(gc, ec), f"{what}: {int((gc != ec).sum())} code bytes differ"
+
+
+def test_tiny_dynamic():
+    x = workloads.tiny_linear().x
+    assert_same(gpu_quantize(x), oracle_expected(x), "tiny")
+
+
+@pytest.mark.parametrize("m,k", [(1, 16), (3, 208), (37, 272), (130, 400), (65, 128), (2, 4112), (513, 96)])
+@pytest.mark.parametrize("static", [False, True])
+def test_ragged_shapes(m, k, static):
+    x = workloads.draw("t3", (m, k), 21, m * 7 + k)
+    gsf = 3.5 if static else None
+    assert_same(gpu_quantize(x, gsf), oracle_expected(x, gsf), f"{m}x{k}")
+
+
+def test_zero_input():
+    x = torch.zeros((5, 64), dtype=torch.bfloat16)
+    got = gpu_quantize(x)
+    assert_same(got, oracle_expected(x), "zeros")
+    assert not got[0].any() and not got[1].any()
+
+
+def test_exhaustive_sweep_unit_scale():
+    """Unit global scale: for every nonzero E4M3 level s a block whose max is exactly
+    6*s forces scale byte s; its other 15 slots sweep every bf16 value with |v| <= 6s."""
+    bits = np.arange(0, 1 << 16, dtype=np.uint32)
+    vals = (bits << 16).view(np.float32)
+    vals = vals[np.isfinite(vals)]
+    rows = []
+    for s8 in range(1, 127):
+        top = np.float32(6.0 * o.E4M3_VALUES[s8])
+        cand = vals[np.abs(vals) <= top]
+        nfill = (-len(cand)) % 15
+        cand = np.concatenate([cand, np.zeros(nfill, np.float32)]).reshape(-1, 15)
+        blocks = np.concatenate([np.full((cand.shape[0], 1), top, np.float32), cand], axis=1)
+        rows.append(blocks)
+    blocks = np.concatenate(rows)
+    pad = (-blocks.shape[0]) % 8
+    blocks = np.concatenate([blocks, np.zeros((pad, 16), np.float32)])
+    x = torch.from_numpy(blocks.reshape(-1, 128)).to(torch.bfloat16)   # 8 blocks per row
+    assert np.array_equal(x.float().numpy().reshape(-1, 16), blocks)   # all exact in bf16
+    got = gpu_quantize(x, 1.0)
+    exp = oracle_expected(x, 1.0)
+    assert_same(got, exp, "sweep")
+    # every level appears as the scale of its own blocks
+    assert set(np.unique(exp[1])) >= set(range(1, 127))
+
+
+def test_weight_quantizer_matches_oracle():
+    for w_cpu in (workloads.tiny_linear().w, workloads.draw("normal", (1024, 5120), 1, 12, 0.02)):
+        w = w_cpu.to(DEV)
+        packed, scales, gsf = nv().quantize_weight(w)
+        torch.cuda.synchronize()
+        pw, sw, gw = o.quantize_weight(w_cpu.float().numpy())
+        n, k = w_cpu.shape
+        assert np.float32(gsf.item()) == gw
+        assert np.array_equal(layout_to_canonical(scales.cpu().numpy(), n, k), sw)
+        assert np.array_equal(packed.cpu().numpy(), pw)
+
+
+@pytest.mark.parametrize("g", [2, 4, 8, 16, 32, 64, 128])
+def test_rotation_bitwise(g):
+    x = workloads.draw("t3", (33, 512), 5, g)
+    y = nv().rotate_activation(x.to(DEV), g)
+    ref = o.rotate_activation(x.float().numpy(), g)
+    assert np.array_equal(y.float().cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    # the fp32 weight fold: f32 -> f32 and f32 -> bf16
+    wf = workloads.draw("normal", (40, 256), 6, g, 0.02).float()
+    y32 = nv().rotate_activation(wf.to(DEV), g)
+    ref32 = o.rotate_activation(wf.numpy(), g, out="f32")
+    assert np.array_equal(y32.cpu().numpy().view(np.uint32), ref32.view(np.uint32))
+    yb = nv().rotate_activation(wf.to(DEV), g, out_dtype=torch.bfloat16)
+    assert np.array_equal(yb.float().cpu().numpy(), o.fold_weight(wf.numpy(), g))
+
+
+@pytest.mark.parametrize("g", [2, 16, 128])
+def test_fused_rotation_equals_rotate_then_quantize(g):
+    x = workloads.draw("t3", (300, 1024), 8, g).to(DEV)
+    fused = nv().quantize_activation(x, None, g)
+    xr = nv().rotate_activation(x, g)
+    split = nv().quantize_activation(xr, None, 0)
+    for a, b in zip(fused, split):
+        assert torch.equal(a, b)
+    assert_same(gpu_quantize(x.cpu(), None, g), oracle_expected(x.cpu(), None, g), f"rot{g}")
+
+
+FULL = [
+    ("qwen3 attention x [4096,5120]", lambda: workloads.qwen3_attention()[0].x, 0),
+    ("qwen3 o_proj x [4096,8192]", lambda: workloads.qwen3_attention()[3].x, 0),
+    ("qwen3 down_proj x silu(g)*u [4096,25600]", lambda: workloads.qwen3_mlp(which=("down",))[0].x, 0),
+    ("vit tile fc_out x t3 [4096,4096] rot16", lambda: workloads.vit_decoder_tiles(tiles=1, which=("fc_out",))[0].x, 16),
+    ("vit tile qkv x t3 [4096,1024] rot16", lambda: workloads.vit_decoder_tiles(tiles=1, which=("qkv",))[0].x, 16),
+]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,make,g", FULL, ids=[f[0].split(" x")[0].replace(" ", "_") for f in FULL])
+def test_full_size_bitwise(name, make, g):
+    print(f"[full-size quantize] {name}", flush=True)
+    x = make()
+    assert_same(gpu_quantize(x, None, g), oracle_expected(x, None, g), name)
+
+
+@pytest.mark.parametrize("m", [1, 16, 128])
+def test_small_m_bitwise(m):
+    for lin in workloads.small_m_sweep(ms=(m,)):
+        if lin.name.endswith(("k_proj", "up_proj")):     # same K as v/gate; keep the sweep short
+            continue
+        assert_same(gpu_quantize(lin.x), oracle_expected(lin.x), lin.name)
