@@ -1,0 +1,327 @@
+// Large-problem NVFP4 GEMM on gfx950: the same product as gemm.hip, tuned for
+// problems with at least one 256 x 256 output tile per compute unit.
+//
+//   out[i, j] = bf16( alpha * sum_b sx[i,b] sw[j,b] sum_{k in b} qx[i,k] qw[j,k] ),
+//   then out = bf16(out + bias[j])
+// ("minimax_h3_nvfp4_decoder" page, nvfp4_linear_inference: mm_fp4 with
+// alpha = 1/(global_sf_x*global_sf_w), then the bias add).
+//
+// One 256-thread workgroup per 256 x 256 tile, one wave per SIMD, each wave 128 x 128
+// (4 x 4 v_mfma_f32_32x32x16_f16 tiles, accumulators in AGPRs).  Expansion of the
+// packed operands to fp16 (gemm_common.h) happens in registers, interleaved with the
+// MFMAs of the previous sub-step, so the matrix core is fed continuously:
+//
+//   * codes go global -> LDS directly (global_load_lds_dwordx4), no register staging;
+//     a 64-byte row of a K tile is four 16-byte chunks, chunk c of row r stored at
+//     slot c ^ (((r >> 1) ^ (r >> 2)) & 3), which keeps the 16-byte LDS reads free
+//     of bank conflicts;
+//   * block scales (8 bytes per row per K tile) go through registers;
+//   * two LDS stages; per 128-wide K tile, eight sub-steps of 16 MFMAs:
+//       0, 1  -                                  2  read the second half of this tile
+//       3  -                                     4  store the next tile's scales
+//       -- LDS barrier: next tile complete in LDS, this tile fully read --
+//       5  read the next tile's first half and scales; issue loads for tile + 2
+//       6  -                                     7  expand the next tile's first step
+//     every sub-step expands the fragments of the following one.
+//   * rows past the end of A or B are clamped to the last row: they only feed output
+//     rows / columns that are never written.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_common.h"
+#include "nvfp4_device.h"
+#include "nvfp4_launch.h"
+
+namespace nvfp4 {
+namespace {
+
+using namespace gemm;
+
+constexpr int kRows = 256;                       // rows of A and of B per tile
+constexpr int kCodeBytes = kRows * 64;           // one operand's codes of one K tile
+constexpr int kScaleBytes = kRows * 8;           // one operand's scales of one K tile
+constexpr int kOffB = kCodeBytes;
+constexpr int kOffAS = 2 * kCodeBytes;
+constexpr int kOffBS = 2 * kCodeBytes + kScaleBytes;
+constexpr int kStage = 2 * kCodeBytes + 2 * kScaleBytes;   // 36 KB
+constexpr int kEpiRowBytes = 128 * 2 + 16;
+constexpr int kLds = 2 * kStage;                            // 72 KB
+static_assert(4 * 32 * kEpiRowBytes <= kLds, "epilogue staging fits in the stages");
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+// Waits for this wave's global and LDS traffic, then the workgroup barrier.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int kMem>
+__device__ __forceinline__ void interleave16() {
+#pragma unroll
+  for (int g = 0; g < 16; ++g) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // one MFMA
+    if (kMem != 0) __builtin_amdgcn_sched_group_barrier(kMem, 1, 0);   // one memory op
+    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);                 // a few VALU
+  }
+  __builtin_amdgcn_sched_barrier(0);   // nothing crosses a sub-step boundary
+}
+
+__global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m, int64_t k,
+    const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, int64_t n,
+    const float* __restrict__ gsf_a, const float* __restrict__ gsf_b, const uint16_t* __restrict__ bias,
+    uint16_t* __restrict__ out, int64_t b_srows, int64_t ldo, int tiles_m, int tiles_n) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a contiguous run
+  // of tiles, M fastest, so the blocks sharing a weight panel share an L2.
+  const int nblk = tiles_m * tiles_n;
+  int bid = blockIdx.x;
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  const int tm = bid % tiles_m;
+  const int tn = bid / tiles_m;
+  const int64_t row0 = (int64_t)tm * kRows;
+  const int64_t col0 = (int64_t)tn * kRows;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // wave-uniform (LDS bases go to M0)
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 31;
+  const int kh = lane >> 5;
+  const int64_t half_k = k / 2;
+  const int64_t kt_count = (k + BK - 1) / BK;
+
+  // Direct loads: wave w, instruction i fills LDS rows 16*(4w+i) .. +15 of an operand;
+  // lane l lands in slot (l & 3) of row 16*(4w+i) + l/4 and so fetches logical chunk
+  // (l & 3) ^ swz(row).
+  const uint8_t* ag[4];
+  const uint8_t* bg[4];
+  int chunk[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * (4 * wave + i) + (lane >> 2);
+    chunk[i] = (lane & 3) ^ swz(r);
+    ag[i] = a_codes + min(row0 + r, m - 1) * half_k + 16 * chunk[i];
+    bg[i] = b_codes + min(col0 + r, n - 1) * half_k + 16 * chunk[i];
+  }
+  const uint8_t* asg = a_scales + min(row0 + t, m - 1) * 8;
+  const uint8_t* bsg = b_scales + min(col0 + t, n - 1) * 8;
+
+  auto stage = [&](int64_t kt) { return lds + (int)(kt & 1) * kStage; };
+
+  // Loads of tile kt into stage kt & 1.  Tiles past the end re-load the last tile (into
+  // a stage that is never consumed), and chunks past the end of a row (last tile when
+  // K % 128 != 0) re-load the row's first chunk: their block scales are the zero
+  // padding of the scale layout, so whatever codes land there contribute nothing.
+  // Both are selects, so the loop body has no branches.
+  auto gload_codes = [&](int64_t kt) {
+    uint8_t* st = stage(kt);
+    const int64_t off = min(kt, kt_count - 1) * 64;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lds_void* la = (lds_void*)(st + (4 * wave + i) * 1024);
+      lds_void* lb = (lds_void*)(st + kOffB + (4 * wave + i) * 1024);
+      const bool in_row = off + 16 * chunk[i] < half_k;
+      const int64_t o = in_row ? off : -16 * chunk[i];
+      __builtin_amdgcn_global_load_lds(ag[i] + o, la, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(bg[i] + o, lb, 16, 0, 0);
+    }
+  };
+  uint2 sa_reg, sb_reg;
+  auto gload_scales = [&](int64_t kt) {
+    const int64_t kc = min(kt, kt_count - 1);
+    sa_reg = *reinterpret_cast<const uint2*>(asg + kc * m * 8);
+    sb_reg = *reinterpret_cast<const uint2*>(bsg + kc * b_srows * 8);
+  };
+  auto sstore_scales = [&](int64_t kt) {
+    uint8_t* st = stage(kt);
+    *reinterpret_cast<uint2*>(st + kOffAS + t * 8) = sa_reg;
+    *reinterpret_cast<uint2*>(st + kOffBS + t * 8) = sb_reg;
+  };
+
+  const int arow = wm * 128 + lr;
+  const int brow = wn * 128 + lr;
+  auto rscale = [&](const uint8_t* st, uint32_t (&as)[4], uint32_t (&bs)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) as[i] = *reinterpret_cast<const uint32_t*>(st + kOffAS + (arow + 32 * i) * 8 + 4 * kh);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bs[j] = *reinterpret_cast<const uint32_t*>(st + kOffBS + (brow + 32 * j) * 8 + 4 * kh);
+  };
+  // half q of the lane's 32 code bytes: logical chunk 2*kh + q
+  auto rhalf = [&](const uint8_t* st, int q, uint4 (&ar)[4], uint4 (&br)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = arow + 32 * i;
+      ar[i] = *reinterpret_cast<const uint4*>(st + r * 64 + 16 * ((2 * kh + q) ^ swz(r)));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = brow + 32 * j;
+      br[j] = *reinterpret_cast<const uint4*>(st + kOffB + r * 64 + 16 * ((2 * kh + q) ^ swz(r)));
+    }
+  };
+  auto expand = [&](const uint4 (&ar)[4], const uint4 (&br)[4], const uint32_t (&as)[4], const uint32_t (&bs)[4],
+                    int step, half8_t (&fa)[4], half8_t (&fb)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = dequant8(word(ar[i], step & 3), scale_pair(as[i], step >> 1));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[j] = dequant8(word(br[j], step & 3), scale_pair(bs[j], step >> 1));
+  };
+
+  float16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  auto mfma16 = [&](const half8_t (&fa)[4], const half8_t (&fb)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+
+  // Prologue: tile 0 complete in stage 0, tile 1 in flight to stage 1.
+  gload_scales(0);
+  gload_codes(0);
+  sstore_scales(0);
+  gload_scales(1);
+  gload_codes(1);
+  stage_barrier();
+  uint32_t asc[4], bsc[4];
+  uint4 ar0[4], br0[4], ar1[4], br1[4];
+  rscale(stage(0), asc, bsc);
+  rhalf(stage(0), 0, ar0, br0);
+  half8_t fa[4], fb[4], na[4], nb[4];
+  expand(ar0, br0, asc, bsc, 0, fa, fb);
+
+  // Every iteration is the same branch-free body (the last two also prepare tiles that
+  // are never multiplied), so each sub-step is one scheduling region.
+#pragma clang loop unroll(disable)
+  for (int64_t kt = 0; kt < kt_count; ++kt) {
+    const uint8_t* cur = stage(kt);
+    const uint8_t* nxt = stage(kt + 1);
+    // sub-step 0
+    expand(ar0, br0, asc, bsc, 1, na, nb);
+    mfma16(fa, fb);
+    interleave16<0>();
+    // sub-step 1
+    expand(ar0, br0, asc, bsc, 2, fa, fb);
+    mfma16(na, nb);
+    interleave16<0>();
+    // sub-step 2
+    rhalf(cur, 1, ar1, br1);
+    expand(ar0, br0, asc, bsc, 3, na, nb);
+    mfma16(fa, fb);
+    interleave16<0x100>();
+    // sub-step 3
+    expand(ar1, br1, asc, bsc, 4, fa, fb);
+    mfma16(na, nb);
+    interleave16<0>();
+    // sub-step 4: the next tile's scales (loaded a tile ago) go to its stage
+    sstore_scales(kt + 1);
+    expand(ar1, br1, asc, bsc, 5, na, nb);
+    mfma16(fa, fb);
+    interleave16<0x200>();
+    stage_barrier();
+    // sub-step 5
+    uint32_t nasc[4], nbsc[4];
+    rscale(nxt, nasc, nbsc);
+    rhalf(nxt, 0, ar0, br0);
+    gload_scales(kt + 2);
+    gload_codes(kt + 2);
+    expand(ar1, br1, asc, bsc, 6, fa, fb);
+    mfma16(na, nb);
+    interleave16<0x100>();
+    // sub-step 6
+    expand(ar1, br1, asc, bsc, 7, na, nb);
+    mfma16(fa, fb);
+    interleave16<0>();
+    // sub-step 7: the next tile's first fragments
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { asc[i] = nasc[i]; bsc[i] = nbsc[i]; }
+    expand(ar0, br0, asc, bsc, 0, fa, fb);
+    mfma16(na, nb);
+    interleave16<0>();
+  }
+  stage_barrier();   // no load still landing in LDS, every wave done with the stages
+
+  // Epilogue: bf16(alpha * acc) staged through LDS 32 rows per wave at a time, then
+  // bf16(y + bias), written as 16-byte row segments.
+  const float alpha = __fdiv_rn(1.0f, __fmul_rn(*gsf_a, *gsf_b));
+  uint8_t* epi = lds + wave * 32 * kEpiRowBytes;
+  const int64_t wrow0 = row0 + wm * 128;
+  const int64_t wcol0 = col0 + wn * 128;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = 8 * (e >> 2) + 4 * kh + (e & 3);
+        const float y = __fmul_rn(alpha, __fmul_rn(acc[i][j][e], kAccUnscale));
+        *reinterpret_cast<uint16_t*>(epi + r * kEpiRowBytes + (j * 32 + lr) * 2) = (uint16_t)f32_to_bf16(y);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int idx = p * 64 + lane;
+      const int r = idx >> 4, sg = idx & 15;
+      const int64_t row = wrow0 + i * 32 + r;
+      const int64_t col = wcol0 + sg * 8;
+      const uint4 v = *reinterpret_cast<const uint4*>(epi + r * kEpiRowBytes + sg * 16);
+      if (row < m && col < n) {
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        if (bias != nullptr) {
+#pragma unroll
+          for (int h = 0; h < 8; ++h) {
+            if (col + h < n) {
+              const uint32_t sh = 16 * (h & 1);
+              const uint32_t zb = add_bias_bf16((w[h >> 1] >> sh) & 0xFFFFu, bias[col + h]);
+              w[h >> 1] = (w[h >> 1] & (0xFFFF0000u >> sh)) | (zb << sh);
+            }
+          }
+        }
+        uint16_t* o = out + row * ldo + col;
+        if (col + 8 <= n && ((uintptr_t)o & 15) == 0) {
+          *reinterpret_cast<uint4*>(o) = make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+          for (int h = 0; h < 8 && col + h < n; ++h) o[h] = (uint16_t)((w[h >> 1] >> (16 * (h & 1))) & 0xFFFFu);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+bool gemm_pipe_supported(int64_t m, int64_t k, int64_t n, const void* a_codes, const void* a_scales,
+                         const void* b_codes, const void* b_scales, int cus) {
+  const int64_t tiles = ((m + kRows - 1) / kRows) * ((n + kRows - 1) / kRows);
+  const bool aligned = (((uintptr_t)a_codes | (uintptr_t)b_codes | (uintptr_t)a_scales | (uintptr_t)b_scales) & 15) == 0;
+  return tiles >= cus && (k / 2) % 16 == 0 && aligned;
+}
+
+hipError_t launch_gemm_pipe(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, int64_t k,
+                            const uint8_t* b_codes, const uint8_t* b_scales, int64_t n, int64_t b_srows, const float* gsf_a,
+                            const float* gsf_b, const uint16_t* bias, uint16_t* out, int64_t ldo, hipStream_t s) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_pipe_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int tiles_m = (int)((m + kRows - 1) / kRows);
+  const int tiles_n = (int)((n + kRows - 1) / kRows);
+  hipLaunchKernelGGL(gemm_pipe_kernel, dim3(tiles_m * tiles_n), dim3(256), kLds, s, a_codes, a_scales, m, k, b_codes,
+                     b_scales, n, gsf_a, gsf_b, bias, out, b_srows, ldo, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -59,6 +59,20 @@ __device__ __forceinline__ uint32_t e2m1_encode(float v) {
   return mag | ((u >> 28) & 8u);
 }
 
+// Eight fp32 values -> eight E2M1 nibbles (value i in bits 4i..4i+3) with the
+// hardware conversion at unit scale, which rounds to nearest even, saturates at 6
+// and keeps the sign exactly like e2m1_encode (checked exhaustively against it on
+// gfx950 around every rounding boundary, for signed zeros, subnormals and
+// out-of-range values).
+__device__ __forceinline__ uint32_t e2m1_encode8(const float* v) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
+  return w;
+}
+
 // Per-16-block quantization, the order every kernel uses:
 //   sf = (gsf * bmax) / 6; s8 = E4M3(sf); s = decode(s8); r = gsf / s; code = E2M1(v * r).
 __device__ __forceinline__ uint32_t block_scale_byte(float gsf, float bmax) {

@@ -28,4 +28,16 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t 
                        const uint8_t* b_codes, const uint8_t* b_scales, int64_t n,
                        const float* gsf_a, const float* gsf_b, const uint16_t* bias, uint16_t* out, hipStream_t s);
 
+// The software-pipelined large-tile GEMM (gemm_pipe.hip): usable when the problem has
+// at least one 256 x 256 tile per compute unit, K is a multiple of 32 and every
+// operand pointer is 16-byte aligned.  It computes output columns [0, n) of a
+// product whose B scale layout holds b_srows rows per K tile and whose output rows
+// are ldo elements apart.
+bool gemm_pipe_supported(int64_t m, int64_t k, int64_t n, const void* a_codes, const void* a_scales,
+                         const void* b_codes, const void* b_scales, int cus);
+hipError_t launch_gemm_pipe(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, int64_t k,
+                            const uint8_t* b_codes, const uint8_t* b_scales, int64_t n, int64_t b_srows,
+                            const float* gsf_a, const float* gsf_b, const uint16_t* bias, uint16_t* out,
+                            int64_t ldo, hipStream_t s);
+
 }  // namespace nvfp4

@@ -19,6 +19,8 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kAmaxBlocks = 512;   // partial maxima of the amax pass (<= kMaxAmaxPartials)
+static_assert(kAmaxBlocks <= kMaxAmaxPartials, "partials buffer");
 
 struct Chunk16 {
   float v[16];
@@ -59,7 +61,10 @@ __device__ __forceinline__ float block_max(float x, float* lds) {
 // Pass 1 of the dynamic scale: every block writes the max |v| of its share of the
 // (optionally rotated, bf16-rounded) input to partials[blockIdx.x].  Lanes take
 // consecutive 16-value chunks, so the lanes holding one rotation group are
-// consecutive and aligned (the group divides the row length).
+// consecutive and aligned (the group divides the row length); each lane keeps
+// kAmaxUnroll chunks in flight.
+constexpr int kAmaxUnroll = 4;
+
 template <bool kRotate>
 __global__ void __launch_bounds__(kThreads) amax_partial_kernel(const uint16_t* __restrict__ x, int64_t n_chunks,
                                                                  int group, float inv_sqrt_g,
@@ -67,33 +72,62 @@ __global__ void __launch_bounds__(kThreads) amax_partial_kernel(const uint16_t* 
   __shared__ float lds[kThreads / 64];
   float m = 0.0f;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t c0 = (int64_t)blockIdx.x * kThreads; c0 < n_chunks; c0 += stride) {
-    const int64_t c = c0 + threadIdx.x;
-    float v[16];
-    if (c < n_chunks) {
-      load16_bf16(x + c * 16, v);
-    } else {
+  for (int64_t c0 = (int64_t)blockIdx.x * kThreads; c0 < n_chunks; c0 += stride * kAmaxUnroll) {
+    float v[kAmaxUnroll][16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = 0.0f;
+    for (int u = 0; u < kAmaxUnroll; ++u) {
+      const int64_t c = c0 + u * stride + threadIdx.x;
+      if (c < n_chunks) {
+        load16_bf16(x + c * 16, v[u]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[u][i] = 0.0f;
+      }
     }
-    if (kRotate) rotate16_bf16(v, group, inv_sqrt_g);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+    for (int u = 0; u < kAmaxUnroll; ++u) {
+      if (kRotate) rotate16_bf16(v[u], group, inv_sqrt_g);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[u][i]));
+    }
   }
   m = block_max(m, lds);
   if (threadIdx.x == 0) partials[blockIdx.x] = m;
 }
 
 // Pass 2: quantize.  Eight consecutive lanes own one 128-wide K tile of one row
-// (lane j of the eight owns the 16-block j of the tile), so each group of eight
-// reads 256 contiguous bytes, writes 64 contiguous code bytes and the 8 scale bytes
-// that are contiguous in the k-tile-major scale layout.
+// (a "unit"; lane j of the eight owns the 16-block j of the tile), so each group of
+// eight reads 256 contiguous bytes and writes 64 contiguous code bytes and the 8
+// scale bytes that are contiguous in the k-tile-major scale layout.  A block takes
+// kQuantUnits rounds of 32 units and loads all of them before computing.
+constexpr int kQuantUnits = 4;
+
 template <bool kRotate>
 __global__ void __launch_bounds__(kThreads) quantize_kernel(
     const uint16_t* __restrict__ x, int64_t m_rows, int64_t k, int group, float inv_sqrt_g,
     const float* __restrict__ static_gsf, const float* __restrict__ partials, int n_partials,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gsf_out) {
   __shared__ float lds[kThreads / 64];
+  const int64_t kt_count = (k + kScaleTileK - 1) / kScaleTileK;
+  const int64_t nb = k / kBlock;
+  const int j = threadIdx.x & 7;
+
+  float v[kQuantUnits][16];
+  int64_t row[kQuantUnits], kt[kQuantUnits];
+#pragma unroll
+  for (int u = 0; u < kQuantUnits; ++u) {
+    const int64_t unit = ((int64_t)blockIdx.x * kQuantUnits + u) * (kThreads / 8) + (threadIdx.x >> 3);
+    row[u] = unit / kt_count;
+    kt[u] = unit - row[u] * kt_count;
+    const int64_t blk = kt[u] * 8 + j;
+    if (row[u] < m_rows && blk < nb) {
+      load16_bf16(x + row[u] * k + blk * kBlock, v[u]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[u][i] = 0.0f;
+    }
+  }
+
   float gsf;
   if (static_gsf != nullptr) {
     gsf = *static_gsf;
@@ -105,42 +139,35 @@ __global__ void __launch_bounds__(kThreads) quantize_kernel(
   }
   if (gsf_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *gsf_out = gsf;
 
-  const int64_t kt_count = (k + kScaleTileK - 1) / kScaleTileK;
-  const int64_t nb = k / kBlock;
-  const int64_t unit = (int64_t)blockIdx.x * (kThreads / 8) + (threadIdx.x >> 3);
-  const int j = threadIdx.x & 7;
-  const int64_t row = unit / kt_count;
-  const int64_t kt = unit - row * kt_count;
-  const int64_t blk = kt * 8 + j;
-  const bool in_row = row < m_rows;
-  const bool valid = in_row && blk < nb;
-
-  float v[16];
-  if (valid) {
-    load16_bf16(x + row * k + blk * kBlock, v);
-  } else {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = 0.0f;
-  }
-  if (kRotate) rotate16_bf16(v, group, inv_sqrt_g);
-
-  float bmax = 0.0f;
+  for (int u = 0; u < kQuantUnits; ++u) {
+    if (kRotate) rotate16_bf16(v[u], group, inv_sqrt_g);
+    const int64_t blk = kt[u] * 8 + j;
+    const bool in_row = row[u] < m_rows;
+    const bool valid = in_row && blk < nb;
+    float bmax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) bmax = fmaxf(bmax, fabsf(v[i]));
-  const uint32_t s8 = block_scale_byte(gsf, bmax);
-  uint32_t w0 = 0, w1 = 0;
-  if (s8 != 0) {
-    const float r = __fdiv_rn(gsf, e4m3_decode(s8));
+    for (int i = 0; i < 16; ++i) bmax = fmaxf(bmax, fabsf(v[u][i]));
+    const uint32_t s8 = valid ? block_scale_byte(gsf, bmax) : 0u;
+    uint32_t w0 = 0, w1 = 0;
+    if (s8 != 0) {
+      const float r = __fdiv_rn(gsf, e4m3_decode(s8));
+      float p[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w0 |= e2m1_encode(__fmul_rn(v[i], r)) << (4 * i);
+      for (int i = 0; i < 16; ++i) p[i] = __fmul_rn(v[u][i], r);
+      w0 = e2m1_encode8(p);
+      w1 = e2m1_encode8(p + 8);
+    }
+    if (valid) *reinterpret_cast<uint2*>(codes + row[u] * (k / 2) + blk * 8) = make_uint2(w0, w1);
+    // gather the unit's 8 scale bytes into lane j == 0 and write them as one 8-byte word
+    uint32_t lo = j < 4 ? s8 << (8 * j) : 0u;
+    uint32_t hi = j >= 4 ? s8 << (8 * (j - 4)) : 0u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w1 |= e2m1_encode(__fmul_rn(v[8 + i], r)) << (4 * i);
-  }
-  if (valid) {
-    *reinterpret_cast<uint2*>(codes + row * (k / 2) + blk * 8) = make_uint2(w0, w1);
-  }
-  if (in_row && kt < kt_count) {
-    scales[(kt * m_rows + row) * 8 + j] = valid ? (uint8_t)s8 : (uint8_t)0;
+    for (int o = 1; o < 8; o <<= 1) {
+      lo |= __shfl_xor(lo, o, 64);
+      hi |= __shfl_xor(hi, o, 64);
+    }
+    if (j == 0 && in_row) *reinterpret_cast<uint2*>(scales + (kt[u] * m_rows + row[u]) * 8) = make_uint2(lo, hi);
   }
 }
 
@@ -213,7 +240,7 @@ int64_t grid_for(int64_t n_chunks, int64_t cap) {
 hipError_t launch_amax_partials(const uint16_t* x, int64_t rows, int64_t k, int group, float inv_sqrt_g,
                                 float* partials, int* n_partials, hipStream_t s) {
   const int64_t n_chunks = rows * k / kBlock;
-  const int grid = (int)grid_for(n_chunks, kMaxAmaxPartials);
+  const int grid = (int)grid_for((n_chunks + kAmaxUnroll - 1) / kAmaxUnroll, kAmaxBlocks);
   *n_partials = grid;
   if (group > 1)
     hipLaunchKernelGGL(amax_partial_kernel<true>, dim3(grid), dim3(kThreads), 0, s, x, n_chunks, group, inv_sqrt_g, partials);
@@ -227,7 +254,8 @@ hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t k, int group
                            uint8_t* codes, uint8_t* scales, float* gsf_out, hipStream_t s) {
   const int64_t kt_count = (k + kScaleTileK - 1) / kScaleTileK;
   const int64_t units = rows * kt_count;
-  const int64_t grid = (units + (kThreads / 8) - 1) / (kThreads / 8);
+  const int64_t per_block = (int64_t)kQuantUnits * (kThreads / 8);
+  const int64_t grid = (units + per_block - 1) / per_block;
   if (group > 1)
     hipLaunchKernelGGL(quantize_kernel<true>, dim3((uint32_t)grid), dim3(kThreads), 0, s, x, rows, k, group, inv_sqrt_g,
                        static_gsf, partials, n_partials, codes, scales, gsf_out);

@@ -53,6 +53,21 @@ def test_random_codes_ragged(m, n, k, with_bias):
     assert_gemm_close(got, ref, bound)
 
 
+@pytest.mark.parametrize("m,n,k", [(4136, 4120, 352), (4096, 4096, 1024), (4097, 4353, 4128)])
+def test_large_tile_path(m, n, k):
+    """Shapes big enough for the software-pipelined 256x256 kernel: ragged M and N
+    (clamped rows), a partial last K tile, and a bias."""
+    rng = np.random.default_rng(m + n + k)
+    px, sx = random_operands(rng, m, k)
+    pw, sw = random_operands(rng, n, k)
+    bias = workloads.draw("normal", (n,), 4, n)
+    got = run_gpu_gemm(px, sx, pw, sw, k, 2.0, 0.5, bias)
+    rows = np.unique(np.concatenate([np.arange(0, 8), np.arange(m - 40, m), rng.choice(m, 200)]))
+    ref = o.nvfp4_gemm(px[rows], sx[rows], pw, sw, o.alpha_of(2.0, 0.5), bias.float().numpy())
+    bound = accumulation_bound(o.dequantize(px[rows], sx[rows]), o.dequantize(pw, sw), o.alpha_of(2.0, 0.5))
+    assert_gemm_close(got[rows], ref, bound)
+
+
 def test_full_scale_range():
     # every E4M3 byte including subnormal scales and zero
     rng = np.random.default_rng(9)
