@@ -93,7 +93,7 @@ def main():
     w = lin.w.to(dev)
     packed, inv_scale, gsf_w = nv.quantize_weight(w)
     del w
-    ws = torch.empty((nv.linear_workspace_bytes(M, K),), dtype=torch.uint8, device=dev)
+    ws = torch.empty((nv.linear_workspace_bytes(M, K, N),), dtype=torch.uint8, device=dev)
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -115,8 +115,10 @@ def main():
     def quant():
         nv.quantize_activation(x)
 
+    gws = torch.empty((max(nv.gemm_workspace_bytes(M, K, N), 1),), dtype=torch.uint8, device=dev)
+
     def gemm():
-        nv.nvfp4_gemm(codes, scales, packed, inv_scale, gsf_x, gsf_w, None, out)
+        nv.nvfp4_gemm(codes, scales, packed, inv_scale, gsf_x, gsf_w, None, out, gws)
 
     for f in (quant, gemm):
         f()

@@ -68,9 +68,16 @@ size_t nvfp4_scale_bytes(int64_t rows, int64_t k);
 /* Workspace nvfp4_quantize_activation / nvfp4_quantize_weight need (amax partials). */
 size_t nvfp4_quantize_workspace_bytes(void);
 
-/* Workspace nvfp4_linear needs for an [m, k] input: activation codes [m][k/2],
- * their scales, amax partials and the activation global scale, each 256-byte aligned. */
-size_t nvfp4_linear_workspace_bytes(int64_t m, int64_t k);
+/* Workspace nvfp4_linear needs for an [m, k] input and n outputs: activation codes
+ * [m][k/2], their scales, amax partials, the activation global scale and the GEMM's
+ * split-K partial sums (nvfp4_gemm_workspace_bytes), each 256-byte aligned.  Depends on
+ * the compute-unit count of the current device. */
+size_t nvfp4_linear_workspace_bytes(int64_t m, int64_t k, int64_t n);
+
+/* Workspace nvfp4_gemm can use for an [m, k] x [n, k] product (fp32 partial sums of
+ * output tiles split along K to fill the GPU); 0 when the product would not split.
+ * Depends on the compute-unit count of the current device. */
+size_t nvfp4_gemm_workspace_bytes(int64_t m, int64_t k, int64_t n);
 
 /*
  * rotate_activation ([DEC] rotate_activation(x, group_size); module docstring).
@@ -115,12 +122,16 @@ int nvfp4_quantize_activation(const void* x_dev, int64_t m, int64_t k,
  * out = bf16(out + bias[j]).  Accumulation is fp32 (order unspecified).
  * x_codes_dev [m][k/2], x_scale_dev (layout above, m rows), packed_dev [n][k/2],
  * inv_scale_dev (n rows), gsf_x_dev / gsf_w_dev fp32 device scalars,
- * bias_dev bf16 [n] or NULL, out_dev bf16 [m][n].
+ * bias_dev bf16 [n] or NULL, out_dev bf16 [m][n].  workspace_dev: NULL, or 256-byte
+ * aligned device memory; with nvfp4_gemm_workspace_bytes(m, k, n) bytes the tiles of
+ * the last partial round are split along K (a deterministic, fixed-order sum), without
+ * it they are not split.  The result is the same function either way (fp32
+ * accumulation order differs).
  */
 int nvfp4_gemm(const uint8_t* x_codes_dev, const uint8_t* x_scale_dev, int64_t m, int64_t k,
                const uint8_t* packed_dev, const uint8_t* inv_scale_dev, int64_t n,
                const float* gsf_x_dev, const float* gsf_w_dev, const void* bias_dev,
-               void* out_dev, void* stream);
+               void* out_dev, void* workspace_dev, size_t workspace_bytes, void* stream);
 
 /*
  * nvfp4_linear ([DEC] nvfp4_linear_inference(x, packed, inv_scale, global_sf_w, bias,
@@ -131,7 +142,7 @@ int nvfp4_gemm(const uint8_t* x_codes_dev, const uint8_t* x_scale_dev, int64_t m
  * [out_features] or NULL.  global_sf_x_dev NULL = dynamic activation scale.
  * rotation_group 0 = none; otherwise the result is bit-identical to
  * nvfp4_linear(rotate_activation(x, g), ..., 0).  out_dev bf16 [m][out_features].
- * workspace: >= nvfp4_linear_workspace_bytes(m, k), 256-byte aligned.
+ * workspace: >= nvfp4_linear_workspace_bytes(m, k, out_features), 256-byte aligned.
  */
 int nvfp4_linear(const void* x_dev, int64_t m, int64_t k,
                  const uint8_t* packed_dev, const uint8_t* inv_scale_dev,

@@ -59,22 +59,27 @@ struct LinearWorkspace {
   uint8_t* scales;
   float* partials;
   float* gsf;
+  void* gemm;
+  size_t gemm_bytes;
   size_t bytes;
 };
 
-LinearWorkspace carve(void* base, int64_t m, int64_t k) {
+LinearWorkspace carve(void* base, int64_t m, int64_t k, int64_t n) {
   // offsets first, pointers only for a real base
   const size_t o_codes = 0;
   const size_t o_scales = align_up(o_codes + (size_t)m * (size_t)(k / 2));
   const size_t o_partials = align_up(o_scales + nvfp4_scale_bytes(m, k));
   const size_t o_gsf = align_up(o_partials + sizeof(float) * nvfp4::kMaxAmaxPartials);
-  LinearWorkspace w{nullptr, nullptr, nullptr, nullptr, align_up(o_gsf + sizeof(float))};
+  const size_t o_gemm = align_up(o_gsf + sizeof(float));
+  const size_t gemm_bytes = nvfp4::gemm_workspace_bytes(m, k, n);
+  LinearWorkspace w{nullptr, nullptr, nullptr, nullptr, nullptr, gemm_bytes, align_up(o_gemm + gemm_bytes)};
   if (base != nullptr) {
     uint8_t* p = static_cast<uint8_t*>(base);
     w.codes = p + o_codes;
     w.scales = p + o_scales;
     w.partials = reinterpret_cast<float*>(p + o_partials);
     w.gsf = reinterpret_cast<float*>(p + o_gsf);
+    w.gemm = gemm_bytes ? p + o_gemm : nullptr;
   }
   return w;
 }
@@ -104,9 +109,14 @@ size_t nvfp4_scale_bytes(int64_t rows, int64_t k) {
 
 size_t nvfp4_quantize_workspace_bytes(void) { return align_up(sizeof(float) * nvfp4::kMaxAmaxPartials); }
 
-size_t nvfp4_linear_workspace_bytes(int64_t m, int64_t k) {
-  if (m < 0 || k <= 0) return 0;
-  return carve(nullptr, m, k).bytes;
+size_t nvfp4_linear_workspace_bytes(int64_t m, int64_t k, int64_t n) {
+  if (m < 0 || k <= 0 || n <= 0) return 0;
+  return carve(nullptr, m, k, n).bytes;
+}
+
+size_t nvfp4_gemm_workspace_bytes(int64_t m, int64_t k, int64_t n) {
+  if (m <= 0 || k <= 0 || n <= 0) return 0;
+  return nvfp4::gemm_workspace_bytes(m, k, n);
 }
 
 const char* nvfp4_last_error(void) { return g_err; }
@@ -162,7 +172,7 @@ int nvfp4_quantize_activation(const void* x, int64_t m, int64_t k, const float* 
 
 int nvfp4_gemm(const uint8_t* x_codes, const uint8_t* x_scale, int64_t m, int64_t k, const uint8_t* packed,
                const uint8_t* inv_scale, int64_t n, const float* gsf_x, const float* gsf_w, const void* bias,
-               void* out, void* stream) {
+               void* out, void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "nvfp4_gemm";
   g_err[0] = 0;
   if (int rc = check_rows_k(fn, m, k, true)) return rc;
@@ -170,9 +180,11 @@ int nvfp4_gemm(const uint8_t* x_codes, const uint8_t* x_scale, int64_t m, int64_
   if (m == 0) return NVFP4_OK;
   if (!x_codes || !x_scale || !packed || !inv_scale || !gsf_x || !gsf_w || !out)
     return fail(NVFP4_ERR_ARG, "%s: NULL tensor argument", fn);
+  if (workspace != nullptr && ((uintptr_t)workspace % NVFP4_WORKSPACE_ALIGN))
+    return fail(NVFP4_ERR_WORKSPACE, "%s: workspace must be %d-byte aligned", fn, NVFP4_WORKSPACE_ALIGN);
   return hip_status(nvfp4::launch_gemm(x_codes, x_scale, m, k, packed, inv_scale, n, gsf_x, gsf_w,
-                                       static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(out),
-                                       static_cast<hipStream_t>(stream)),
+                                       static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(out), workspace,
+                                       workspace != nullptr ? workspace_bytes : 0, static_cast<hipStream_t>(stream)),
                     fn);
 }
 
@@ -187,16 +199,17 @@ int nvfp4_linear(const void* x, int64_t m, int64_t k, const uint8_t* packed, con
     return fail(NVFP4_ERR_SHAPE, "%s: out_features must be in [1, 2^31), got %lld", fn, (long long)out_features);
   if (m == 0) return NVFP4_OK;
   if (!x || !packed || !inv_scale || !global_sf_w || !out) return fail(NVFP4_ERR_ARG, "%s: NULL tensor argument", fn);
-  const size_t need = nvfp4_linear_workspace_bytes(m, k);
+  const size_t need = nvfp4_linear_workspace_bytes(m, k, out_features);
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % NVFP4_WORKSPACE_ALIGN))
     return fail(NVFP4_ERR_WORKSPACE, "%s: need a %d-byte aligned workspace of %zu bytes, got %zu", fn,
                 NVFP4_WORKSPACE_ALIGN, need, workspace_bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const LinearWorkspace ws = carve(workspace, m, k);
+  const LinearWorkspace ws = carve(workspace, m, k, out_features);
   if (int rc = quantize_impl(fn, x, m, k, global_sf_x, rotation_group, ws.codes, ws.scales, ws.gsf, ws.partials, s))
     return rc;
   return hip_status(nvfp4::launch_gemm(ws.codes, ws.scales, m, k, packed, inv_scale, out_features, ws.gsf,
-                                       global_sf_w, static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(out), s),
+                                       global_sf_w, static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(out),
+                                       ws.gemm, ws.gemm_bytes, s),
                     fn);
 }
 

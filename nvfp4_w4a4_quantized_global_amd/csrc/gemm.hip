@@ -311,6 +311,8 @@ hipError_t launch_generic(const uint8_t* a_codes, const uint8_t* a_scales, int64
                                 aligned16, s);
 }
 
+}  // namespace
+
 int compute_units() {
   static int cached[64] = {0};
   int dev = 0;
@@ -323,27 +325,19 @@ int compute_units() {
   return cached[dev];
 }
 
-}  // namespace
+size_t gemm_workspace_bytes(int64_t m, int64_t k, int64_t n) {
+  if ((k / 2) % 16 != 0 || m < 512) return 0;
+  return gemm_pipe_workspace_bytes(m, k, n, compute_units());
+}
 
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, int64_t k,
                        const uint8_t* b_codes, const uint8_t* b_scales, int64_t n,
-                       const float* gsf_a, const float* gsf_b, const uint16_t* bias, uint16_t* out, hipStream_t s) {
+                       const float* gsf_a, const float* gsf_b, const uint16_t* bias, uint16_t* out,
+                       void* workspace, size_t workspace_bytes, hipStream_t s) {
   const int cus = compute_units();
-  if (gemm_pipe_supported(m, k, n, a_codes, a_scales, b_codes, b_scales, cus)) {
-    // Large-tile kernel over whole rounds of 256 x 256 tiles (tiles run M fastest, so a
-    // whole number of rounds that is also whole tile columns); the columns left over
-    // go to the generic kernel in one more round of smaller tiles.
-    const int64_t tiles_m = (m + 255) / 256;
-    const int64_t tiles_n = (n + 255) / 256;
-    const int64_t full = (tiles_m * tiles_n) / cus * cus;
-    int64_t cols = full / tiles_m;
-    if (cols >= tiles_n || (tiles_m * tiles_n) % cus == 0) cols = tiles_n;
-    const int64_t n_main = cols == tiles_n ? n : cols * 256;
-    hipError_t e = launch_gemm_pipe(a_codes, a_scales, m, k, b_codes, b_scales, n_main, n, gsf_a, gsf_b, bias, out, n, s);
-    if (e != hipSuccess || n_main == n) return e;
-    return launch_generic(a_codes, a_scales, m, k, b_codes + n_main * (k / 2), b_scales + n_main * 8, n - n_main,
-                          gsf_a, gsf_b, bias != nullptr ? bias + n_main : nullptr, out + n_main, n, n, cus, s);
-  }
+  if (gemm_pipe_supported(m, k, n, a_codes, a_scales, b_codes, b_scales, cus))
+    return launch_gemm_pipe(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, out, workspace,
+                            workspace_bytes, cus, s);
   return launch_generic(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, out, n, n, cus, s);
 }
 

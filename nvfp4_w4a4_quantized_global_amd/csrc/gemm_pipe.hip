@@ -72,13 +72,22 @@ __global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m, int64_t k,
     const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, int64_t n,
     const float* __restrict__ gsf_a, const float* __restrict__ gsf_b, const uint16_t* __restrict__ bias,
-    uint16_t* __restrict__ out, int64_t b_srows, int64_t ldo, int tiles_m, int tiles_n) {
+    uint16_t* __restrict__ out, int64_t b_srows, int64_t ldo, int tiles_m, int tiles_n, int tile0, int splits,
+    float* __restrict__ partial) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a contiguous run
-  // of tiles, M fastest, so the blocks sharing a weight panel share an L2.
-  const int nblk = tiles_m * tiles_n;
+  // Tiles run M fastest.  Without split-K, workgroups (dealt round-robin to the 8 XCDs)
+  // are remapped so each XCD gets a contiguous run of tiles: blocks sharing a weight
+  // panel share an L2.  With split-K, block b takes K range b % splits of tile b / splits.
+  const int nblk = gridDim.x;
   int bid = blockIdx.x;
-  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  int split = 0;
+  if (splits > 1) {
+    split = bid % splits;
+    bid = bid / splits;
+  } else if ((nblk & 7) == 0) {
+    bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  }
+  bid += tile0;
   const int tm = bid % tiles_m;
   const int tn = bid / tiles_m;
   const int64_t row0 = (int64_t)tm * kRows;
@@ -91,7 +100,9 @@ __global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
   const int lr = lane & 31;
   const int kh = lane >> 5;
   const int64_t half_k = k / 2;
-  const int64_t kt_count = (k + BK - 1) / BK;
+  const int64_t kt_all = (k + BK - 1) / BK;
+  const int64_t kt_begin = kt_all * split / splits;        // this block's K tiles
+  const int64_t kt_end = kt_all * (split + 1) / splits;
 
   // Direct loads: wave w, instruction i fills LDS rows 16*(4w+i) .. +15 of an operand;
   // lane l lands in slot (l & 3) of row 16*(4w+i) + l/4 and so fetches logical chunk
@@ -118,7 +129,7 @@ __global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
   // Both are selects, so the loop body has no branches.
   auto gload_codes = [&](int64_t kt) {
     uint8_t* st = stage(kt);
-    const int64_t off = min(kt, kt_count - 1) * 64;
+    const int64_t off = min(kt, kt_end - 1) * 64;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       lds_void* la = (lds_void*)(st + (4 * wave + i) * 1024);
@@ -131,7 +142,7 @@ __global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
   };
   uint2 sa_reg, sb_reg;
   auto gload_scales = [&](int64_t kt) {
-    const int64_t kc = min(kt, kt_count - 1);
+    const int64_t kc = min(kt, kt_end - 1);
     sa_reg = *reinterpret_cast<const uint2*>(asg + kc * m * 8);
     sb_reg = *reinterpret_cast<const uint2*>(bsg + kc * b_srows * 8);
   };
@@ -184,24 +195,24 @@ __global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
       for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
   };
 
-  // Prologue: tile 0 complete in stage 0, tile 1 in flight to stage 1.
-  gload_scales(0);
-  gload_codes(0);
-  sstore_scales(0);
-  gload_scales(1);
-  gload_codes(1);
+  // Prologue: the first K tile complete in its stage, the second in flight.
+  gload_scales(kt_begin);
+  gload_codes(kt_begin);
+  sstore_scales(kt_begin);
+  gload_scales(kt_begin + 1);
+  gload_codes(kt_begin + 1);
   stage_barrier();
   uint32_t asc[4], bsc[4];
   uint4 ar0[4], br0[4], ar1[4], br1[4];
-  rscale(stage(0), asc, bsc);
-  rhalf(stage(0), 0, ar0, br0);
+  rscale(stage(kt_begin), asc, bsc);
+  rhalf(stage(kt_begin), 0, ar0, br0);
   half8_t fa[4], fb[4], na[4], nb[4];
   expand(ar0, br0, asc, bsc, 0, fa, fb);
 
   // Every iteration is the same branch-free body (the last two also prepare tiles that
   // are never multiplied), so each sub-step is one scheduling region.
 #pragma clang loop unroll(disable)
-  for (int64_t kt = 0; kt < kt_count; ++kt) {
+  for (int64_t kt = kt_begin; kt < kt_end; ++kt) {
     const uint8_t* cur = stage(kt);
     const uint8_t* nxt = stage(kt + 1);
     // sub-step 0
@@ -248,6 +259,20 @@ __global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
     interleave16<0>();
   }
   stage_barrier();   // no load still landing in LDS, every wave done with the stages
+
+  if (splits > 1) {
+    // Split-K: the raw fp32 accumulators of this K range, in register order (entry q of
+    // thread t at ((split * tiles + tile) * 256 + q) * 256 + t); split_k_reduce finishes.
+    const int tiles = gridDim.x / splits;
+    float* p = partial + ((int64_t)split * tiles + blockIdx.x / splits) * 65536 + t;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) p[((i * 4 + j) * 16 + e) * 256] = acc[i][j][e];
+    return;
+  }
 
   // Epilogue: bf16(alpha * acc) staged through LDS 32 rows per wave at a time, then
   // bf16(y + bias), written as 16-byte row segments.
@@ -298,18 +323,77 @@ __global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
   }
 }
 
+// Sums the split-K partials of `tiles` tiles (starting at tile index tile0) in split
+// order, then applies the epilogue of the main kernel: bf16(alpha * acc), then the bias.
+__global__ void __launch_bounds__(256) split_k_reduce(const float* __restrict__ partial, int splits, int tiles,
+                                                      int tile0, int tiles_m, int64_t m, int64_t n,
+                                                      const float* __restrict__ gsf_a, const float* __restrict__ gsf_b,
+                                                      const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
+                                                      int64_t ldo) {
+  const int tl = blockIdx.x >> 8;         // tile within the split launch
+  const int q = blockIdx.x & 255;         // accumulator entry (i, j, e) of the owning thread
+  const int t = threadIdx.x;              // owning thread of the main kernel
+  float acc = 0.0f;
+  for (int sp = 0; sp < splits; ++sp) acc += partial[(((int64_t)sp * tiles + tl) * 256 + q) * 256 + t];
+  const int tile = tile0 + tl;
+  const int64_t row0 = (int64_t)(tile % tiles_m) * kRows;
+  const int64_t col0 = (int64_t)(tile / tiles_m) * kRows;
+  const int wave = t >> 6, lane = t & 63;
+  const int i = q >> 6, j = (q >> 4) & 3, e = q & 15;
+  const int64_t row = row0 + (wave >> 1) * 128 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+  const int64_t col = col0 + (wave & 1) * 128 + j * 32 + (lane & 31);
+  if (row >= m || col >= n) return;
+  const float alpha = __fdiv_rn(1.0f, __fmul_rn(*gsf_a, *gsf_b));
+  uint32_t y = f32_to_bf16(__fmul_rn(alpha, __fmul_rn(acc, kAccUnscale)));
+  if (bias != nullptr) y = add_bias_bf16(y, bias[col]);
+  out[row * ldo + col] = (uint16_t)y;
+}
+
+// How a problem is cut: `full` tiles in whole rounds of one tile per compute unit,
+// then `rest` tiles, each split `splits` ways along K when that fills the GPU better
+// and the workspace allows it.
+struct PipePlan {
+  int64_t tiles_m, tiles_n, full, rest;
+  int splits;
+};
+
+PipePlan pipe_plan(int64_t m, int64_t k, int64_t n, int cus) {
+  PipePlan p;
+  p.tiles_m = (m + kRows - 1) / kRows;
+  p.tiles_n = (n + kRows - 1) / kRows;
+  const int64_t tiles = p.tiles_m * p.tiles_n;
+  p.full = tiles / cus * cus;
+  p.rest = tiles - p.full;
+  p.splits = 1;
+  const int64_t kt = (k + BK - 1) / BK;
+  if (p.rest > 0) {
+    int64_t sp = cus / p.rest;
+    if (sp > 4) sp = 4;
+    while (sp > 1 && kt < 2 * sp) --sp;     // keep at least two K tiles per split
+    p.splits = (int)(sp < 1 ? 1 : sp);
+  }
+  return p;
+}
+
 }  // namespace
 
 bool gemm_pipe_supported(int64_t m, int64_t k, int64_t n, const void* a_codes, const void* a_scales,
                          const void* b_codes, const void* b_scales, int cus) {
-  const int64_t tiles = ((m + kRows - 1) / kRows) * ((n + kRows - 1) / kRows);
+  (void)n;
+  (void)cus;
   const bool aligned = (((uintptr_t)a_codes | (uintptr_t)b_codes | (uintptr_t)a_scales | (uintptr_t)b_scales) & 15) == 0;
-  return tiles >= cus && (k / 2) % 16 == 0 && aligned;
+  return m >= 2 * kRows && (k / 2) % 16 == 0 && aligned;
+}
+
+size_t gemm_pipe_workspace_bytes(int64_t m, int64_t k, int64_t n, int cus) {
+  const PipePlan p = pipe_plan(m, k, n, cus);
+  return p.splits > 1 ? (size_t)p.splits * (size_t)p.rest * 65536u * sizeof(float) : 0;
 }
 
 hipError_t launch_gemm_pipe(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, int64_t k,
-                            const uint8_t* b_codes, const uint8_t* b_scales, int64_t n, int64_t b_srows, const float* gsf_a,
-                            const float* gsf_b, const uint16_t* bias, uint16_t* out, int64_t ldo, hipStream_t s) {
+                            const uint8_t* b_codes, const uint8_t* b_scales, int64_t n, const float* gsf_a,
+                            const float* gsf_b, const uint16_t* bias, uint16_t* out, void* workspace,
+                            size_t workspace_bytes, int cus, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_pipe_kernel),
@@ -317,10 +401,25 @@ hipError_t launch_gemm_pipe(const uint8_t* a_codes, const uint8_t* a_scales, int
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int tiles_m = (int)((m + kRows - 1) / kRows);
-  const int tiles_n = (int)((n + kRows - 1) / kRows);
-  hipLaunchKernelGGL(gemm_pipe_kernel, dim3(tiles_m * tiles_n), dim3(256), kLds, s, a_codes, a_scales, m, k, b_codes,
-                     b_scales, n, gsf_a, gsf_b, bias, out, b_srows, ldo, tiles_m, tiles_n);
+  PipePlan p = pipe_plan(m, k, n, cus);
+  const size_t need = p.splits > 1 ? (size_t)p.splits * (size_t)p.rest * 65536u * sizeof(float) : 0;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) p.splits = 1;
+  const int tm = (int)p.tiles_m, tn = (int)p.tiles_n;
+  if (p.full > 0) {
+    hipLaunchKernelGGL(gemm_pipe_kernel, dim3((uint32_t)p.full), dim3(256), kLds, s, a_codes, a_scales, m, k, b_codes,
+                       b_scales, n, gsf_a, gsf_b, bias, out, n, n, tm, tn, 0, 1, (float*)nullptr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.rest == 0) return hipSuccess;
+  float* partial = static_cast<float*>(workspace);
+  hipLaunchKernelGGL(gemm_pipe_kernel, dim3((uint32_t)(p.rest * p.splits)), dim3(256), kLds, s, a_codes, a_scales, m, k,
+                     b_codes, b_scales, n, gsf_a, gsf_b, bias, out, n, n, tm, tn, (int)p.full, p.splits,
+                     p.splits > 1 ? partial : (float*)nullptr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.splits == 1) return e;
+  hipLaunchKernelGGL(split_k_reduce, dim3((uint32_t)(p.rest * 256)), dim3(256), 0, s, partial, p.splits, (int)p.rest,
+                     (int)p.full, tm, m, n, gsf_a, gsf_b, bias, out, n);
   return hipGetLastError();
 }
 

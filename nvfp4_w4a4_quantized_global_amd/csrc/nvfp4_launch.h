@@ -26,18 +26,25 @@ hipError_t launch_scale_layout(const uint8_t* src, uint8_t* dst, int64_t rows, i
 
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, int64_t k,
                        const uint8_t* b_codes, const uint8_t* b_scales, int64_t n,
-                       const float* gsf_a, const float* gsf_b, const uint16_t* bias, uint16_t* out, hipStream_t s);
+                       const float* gsf_a, const float* gsf_b, const uint16_t* bias, uint16_t* out,
+                       void* workspace, size_t workspace_bytes, hipStream_t s);
 
-// The software-pipelined large-tile GEMM (gemm_pipe.hip): usable when the problem has
-// at least one 256 x 256 tile per compute unit, K is a multiple of 32 and every
-// operand pointer is 16-byte aligned.  It computes output columns [0, n) of a
-// product whose B scale layout holds b_srows rows per K tile and whose output rows
-// are ldo elements apart.
+// Compute units of the current device (cached per device).
+int compute_units();
+
+// The software-pipelined 256 x 256-tile GEMM (gemm_pipe.hip): used for M >= 512 when K
+// is a multiple of 32 and every operand pointer is 16-byte aligned.  Tiles beyond the
+// last whole round (one tile per compute unit) are split along K when the workspace
+// (gemm_pipe_workspace_bytes) allows; without it they run unsplit.
 bool gemm_pipe_supported(int64_t m, int64_t k, int64_t n, const void* a_codes, const void* a_scales,
                          const void* b_codes, const void* b_scales, int cus);
+size_t gemm_pipe_workspace_bytes(int64_t m, int64_t k, int64_t n, int cus);
 hipError_t launch_gemm_pipe(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, int64_t k,
-                            const uint8_t* b_codes, const uint8_t* b_scales, int64_t n, int64_t b_srows,
-                            const float* gsf_a, const float* gsf_b, const uint16_t* bias, uint16_t* out,
-                            int64_t ldo, hipStream_t s);
+                            const uint8_t* b_codes, const uint8_t* b_scales, int64_t n, const float* gsf_a,
+                            const float* gsf_b, const uint16_t* bias, uint16_t* out, void* workspace,
+                            size_t workspace_bytes, int cus, hipStream_t s);
+
+// Workspace the GEMM dispatcher can use for an [m, k] x [n, k] product (0 if none).
+size_t gemm_workspace_bytes(int64_t m, int64_t k, int64_t n);
 
 }  // namespace nvfp4

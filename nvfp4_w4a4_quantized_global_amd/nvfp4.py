@@ -49,8 +49,14 @@ def scale_bytes(rows: int, k: int) -> int:
     return int(lib().nvfp4_scale_bytes(rows, k))
 
 
-def linear_workspace_bytes(m: int, k: int) -> int:
-    return int(lib().nvfp4_linear_workspace_bytes(m, k))
+def linear_workspace_bytes(m: int, k: int, n: int) -> int:
+    """Workspace of nvfp4_linear for an [m, k] input and n outputs (current device)."""
+    return int(lib().nvfp4_linear_workspace_bytes(m, k, n))
+
+
+def gemm_workspace_bytes(m: int, k: int, n: int) -> int:
+    """Workspace nvfp4_gemm can use to split the last round of tiles along K (current device)."""
+    return int(lib().nvfp4_gemm_workspace_bytes(m, k, n))
 
 
 def quantize_workspace_bytes() -> int:
@@ -114,9 +120,12 @@ def quantize_activation(x: torch.Tensor, global_sf_x=None, rotation_group: int =
 
 
 def nvfp4_gemm(x_codes: torch.Tensor, x_scales: torch.Tensor, packed: torch.Tensor, inv_scale: torch.Tensor,
-               global_sf_x, global_sf_w, bias: torch.Tensor | None = None, out: torch.Tensor | None = None
-               ) -> torch.Tensor:
-    """Block-scaled GEMM on already quantized activations; bf16 [M, N]."""
+               global_sf_x, global_sf_w, bias: torch.Tensor | None = None, out: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None, split_k: bool = True) -> torch.Tensor:
+    """Block-scaled GEMM on already quantized activations; bf16 [M, N].
+
+    With ``split_k`` (default) a workspace of gemm_workspace_bytes is used (allocated
+    here if not given) so the last partial round of tiles is split along K."""
     _require_cuda("x_codes", x_codes, torch.uint8, 2)
     _require_cuda("packed", packed, torch.uint8, 2)
     m, half_k = x_codes.shape
@@ -136,8 +145,16 @@ def nvfp4_gemm(x_codes: torch.Tensor, x_scales: torch.Tensor, packed: torch.Tens
             raise ValueError(f"bias must have {n} elements, got {bias.numel()}")
     if out is None:
         out = torch.empty((m, n), dtype=torch.bfloat16, device=x_codes.device)
+    ws_bytes = 0
+    if split_k:
+        need = gemm_workspace_bytes(m, k, n)
+        if need and (workspace is None or workspace.numel() < need):
+            workspace = torch.empty((need,), dtype=torch.uint8, device=x_codes.device)
+        ws_bytes = 0 if workspace is None else workspace.numel()
+    else:
+        workspace = None
     check(lib().nvfp4_gemm(_ptr(x_codes), _ptr(x_scales), m, k, _ptr(packed), _ptr(inv_scale), n, _ptr(gx), _ptr(gw),
-                           _ptr(bias), _ptr(out), _stream(x_codes.device)))
+                           _ptr(bias), _ptr(out), _ptr(workspace), ws_bytes, _stream(x_codes.device)))
     return out
 
 
@@ -171,7 +188,7 @@ def nvfp4_linear(x: torch.Tensor, packed: torch.Tensor, inv_scale: torch.Tensor,
         if bias.numel() != out_features:
             raise ValueError(f"bias must have {out_features} elements, got {bias.numel()}")
     m = x2d.shape[0]
-    need = linear_workspace_bytes(m, k)
+    need = linear_workspace_bytes(m, k, out_features)
     if workspace is None:
         workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
     if out is None:

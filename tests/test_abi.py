@@ -38,8 +38,12 @@ def test_sizes():
     assert L.nvfp4_scale_bytes(3, 208) == 2 * 3 * 8           # K % 128 != 0: padded tile
     assert L.nvfp4_scale_bytes(0, 256) == 0
     assert L.nvfp4_quantize_workspace_bytes() % 256 == 0 and L.nvfp4_quantize_workspace_bytes() >= 4096
-    ws = L.nvfp4_linear_workspace_bytes(4096, 5120)
+    ws = L.nvfp4_linear_workspace_bytes(4096, 5120, 1024)
     assert ws >= 4096 * 2560 + 40 * 4096 * 8 + 4096 + 4 and ws % 256 == 0
+    # 64 tiles of 256x256 on 256 CUs split four ways: 4 * 64 fp32 tiles of partials
+    assert L.nvfp4_gemm_workspace_bytes(4096, 5120, 1024) == 4 * 64 * 65536 * 4
+    assert L.nvfp4_gemm_workspace_bytes(4096, 5120, 16384) == 0      # whole rounds only
+    assert L.nvfp4_gemm_workspace_bytes(100, 5120, 1024) == 0        # small M: no split
 
 
 def _msg():
@@ -70,7 +74,7 @@ def test_rotation_group_must_divide_k():
 
 def test_out_features_and_workspace():
     assert lib().nvfp4_linear(FAKE, 4, 64, FAKE, FAKE, FAKE, None, 0, None, 0, FAKE, FAKE, 1 << 20, None) == NVFP4_ERR_SHAPE
-    need = lib().nvfp4_linear_workspace_bytes(4, 64)
+    need = lib().nvfp4_linear_workspace_bytes(4, 64, 8)
     rc = lib().nvfp4_linear(FAKE, 4, 64, FAKE, FAKE, FAKE, None, 8, None, 0, FAKE, FAKE, need - 1, None)
     assert rc == NVFP4_ERR_WORKSPACE
     rc = lib().nvfp4_linear(FAKE, 4, 64, FAKE, FAKE, FAKE, None, 8, None, 0, FAKE, ctypes.c_void_p(0x1010), need, None)

@@ -68,6 +68,30 @@ def test_large_tile_path(m, n, k):
     assert_gemm_close(got[rows], ref, bound)
 
 
+@pytest.mark.parametrize("m,n,k", [(4096, 1024, 5120), (4096, 5120, 1024), (1000, 3000, 640)])
+def test_split_k_tail(m, n, k):
+    """Tiles past the last whole round are split along K into a workspace and summed in a
+    fixed order: same oracle tolerance, bitwise repeatable, and close to the unsplit run."""
+    rng = np.random.default_rng(m * 3 + n + k)
+    px, sx = random_operands(rng, m, k)
+    pw, sw = random_operands(rng, n, k)
+    bias = workloads.draw("normal", (n,), 5, n)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    args = (t(px), t(canonical_to_layout(sx, k)), t(pw), t(canonical_to_layout(sw, k)), 2.0, 0.5, bias.to(DEV))
+    a = nv().nvfp4_gemm(*args)
+    b = nv().nvfp4_gemm(*args)
+    c = nv().nvfp4_gemm(*args, split_k=False)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    got = a.float().cpu().numpy()
+    rows = np.unique(np.concatenate([np.arange(m - 8, m), rng.choice(m, 120)]))
+    alpha = o.alpha_of(2.0, 0.5)
+    ref = o.nvfp4_gemm(px[rows], sx[rows], pw, sw, alpha, bias.float().numpy())
+    bound = accumulation_bound(o.dequantize(px[rows], sx[rows]), o.dequantize(pw, sw), alpha)
+    assert_gemm_close(got[rows], ref, bound)
+    assert_gemm_close(c.float().cpu().numpy()[rows], ref, bound)
+
+
 def test_full_scale_range():
     # every E4M3 byte including subnormal scales and zero
     rng = np.random.default_rng(9)
