@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB_NAME = "libnvfp4.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ("api.hip", "quantize.hip", "gemm.hip", "gemm_pipe.hip")
+SOURCES = ("api.hip", "quantize.hip", "gemm.hip", "gemm_pipe.hip", "gemm_skinny.hip")
 ARCH = "gfx950"
 
 # -ffp-contract=off: the quantizer's multiply/divide sequence must round like the

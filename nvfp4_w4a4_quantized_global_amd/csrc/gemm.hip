@@ -325,8 +325,18 @@ int compute_units() {
   return cached[dev];
 }
 
+namespace {
+
+// Kernel choice by shape (operands aligned, K a multiple of 32): weight streaming while
+// the activation rows fit one pass of the weight (M <= 64, or M <= 128 with a narrow
+// weight), the pipelined 256 x 256 kernel above that.
+bool prefer_skinny(int64_t m, int64_t n) { return m <= 64 || (m <= 128 && n < 4096); }
+
+}  // namespace
+
 size_t gemm_workspace_bytes(int64_t m, int64_t k, int64_t n) {
-  if ((k / 2) % 16 != 0 || m < 512) return 0;
+  if ((k / 2) % 16 != 0) return 0;
+  if (prefer_skinny(m, n)) return gemm_skinny_workspace_bytes(m, k, n, compute_units());
   return gemm_pipe_workspace_bytes(m, k, n, compute_units());
 }
 
@@ -335,6 +345,9 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t 
                        const float* gsf_a, const float* gsf_b, const uint16_t* bias, uint16_t* out,
                        void* workspace, size_t workspace_bytes, hipStream_t s) {
   const int cus = compute_units();
+  if (prefer_skinny(m, n) && gemm_skinny_supported(m, k, a_codes, a_scales, b_codes, b_scales))
+    return launch_gemm_skinny(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, out, workspace,
+                              workspace_bytes, cus, s);
   if (gemm_pipe_supported(m, k, n, a_codes, a_scales, b_codes, b_scales, cus))
     return launch_gemm_pipe(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, out, workspace,
                             workspace_bytes, cus, s);

@@ -367,8 +367,7 @@ PipePlan pipe_plan(int64_t m, int64_t k, int64_t n, int cus) {
   p.splits = 1;
   const int64_t kt = (k + BK - 1) / BK;
   if (p.rest > 0) {
-    int64_t sp = cus / p.rest;
-    if (sp > 4) sp = 4;
+    int64_t sp = cus / p.rest;              // at most one round: partials <= cus tiles
     while (sp > 1 && kt < 2 * sp) --sp;     // keep at least two K tiles per split
     p.splits = (int)(sp < 1 ? 1 : sp);
   }
@@ -379,10 +378,11 @@ PipePlan pipe_plan(int64_t m, int64_t k, int64_t n, int cus) {
 
 bool gemm_pipe_supported(int64_t m, int64_t k, int64_t n, const void* a_codes, const void* a_scales,
                          const void* b_codes, const void* b_scales, int cus) {
+  (void)m;
   (void)n;
   (void)cus;
   const bool aligned = (((uintptr_t)a_codes | (uintptr_t)b_codes | (uintptr_t)a_scales | (uintptr_t)b_scales) & 15) == 0;
-  return m >= 2 * kRows && (k / 2) % 16 == 0 && aligned;
+  return (k / 2) % 16 == 0 && aligned;
 }
 
 size_t gemm_pipe_workspace_bytes(int64_t m, int64_t k, int64_t n, int cus) {

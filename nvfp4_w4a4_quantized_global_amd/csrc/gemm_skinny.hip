@@ -1,0 +1,253 @@
+// NVFP4 GEMM for few activation rows (M <= 128): weight streaming.
+//
+// Same product as gemm.hip ("minimax_h3_nvfp4_decoder" page, nvfp4_linear_inference:
+// mm_fp4 with alpha = 1/(global_sf_x*global_sf_w), then the bias add), for the decode
+// shapes where the packed weight (N*K/2 code bytes + N*K/16 scale bytes) is the traffic
+// that matters: every weight byte is read from HBM exactly once, the activation codes
+// come from L2.
+//
+// Work: a block owns 64 output columns (weight rows) and a range of 256-wide K super
+// tiles (two tiles of the scale layout); its four waves take the super tiles
+// round-robin and their fp32 results are summed through LDS in wave order.  When that
+// leaves too few blocks to fill the GPU, the K range is also split across blocks (fp32
+// partials in a workspace, summed in split order by gemm_skinny_reduce), so results
+// are bitwise repeatable.
+//
+// Operands are expanded to fp16 exactly (gemm_common.h) and multiplied on
+// v_mfma_f32_16x16x32_f16.  In every MFMA, lane group g = lane / 16 supplies K values
+// [64g + 8s, +8) of the super tile at sub-step s for both operands (a consistent
+// permutation of K), so each lane loads 32 contiguous code bytes per row and the 16
+// lanes of a row together read its whole 128-byte line.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_common.h"
+#include "nvfp4_device.h"
+#include "nvfp4_launch.h"
+
+namespace nvfp4 {
+namespace {
+
+using namespace gemm;
+
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kCols = 64;            // output columns per block (4 MFMA tiles of 16)
+constexpr int kWaves = 4;
+
+template <int MT>   // M tiles of 16 rows
+__global__ void __launch_bounds__(256) gemm_skinny_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m, int64_t k,
+    const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, int64_t n,
+    const float* __restrict__ gsf_a, const float* __restrict__ gsf_b, const uint16_t* __restrict__ bias,
+    uint16_t* __restrict__ out, int splits, float* __restrict__ partial) {
+  __shared__ float red[MT * 4][4][64];     // waves 1..3 hand their sums to wave 0, one at a time
+
+  const int col_group = blockIdx.x / splits;
+  const int split = blockIdx.x % splits;
+  const int64_t n0 = (int64_t)col_group * kCols;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+  const int64_t half_k = k / 2;
+  const int64_t kt_all = (k + BK - 1) / BK;
+  const int64_t st_all = (kt_all + 1) / 2;                 // 256-wide super tiles
+  const int64_t st_begin = st_all * split / splits;
+  const int64_t st_end = st_all * (split + 1) / splits;
+
+  // Row pointers (rows past the end clamp to the last row; their outputs are dropped).
+  const uint8_t* brow[4];
+  const uint8_t* bsrow[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t r = min(n0 + 16 * j + l16, n - 1);
+    brow[j] = b_codes + r * half_k;
+    bsrow[j] = b_scales + r * 8 + 4 * (g & 1);
+  }
+  const uint8_t* arow[MT];
+  const uint8_t* asrow[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int64_t r = min((int64_t)(16 * i + l16), m - 1);
+    arow[i] = a_codes + r * half_k;
+    asrow[i] = a_scales + r * 8 + 4 * (g & 1);
+  }
+
+  float4_t acc[MT][4];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // One 256-wide K super tile (two scale-layout tiles) per wave and iteration, so each
+  // row's 128 code bytes (a whole cache line) are read by one instruction.  Lane group g
+  // takes K values [64g, 64g + 64) of the super tile: 32 code bytes and the 4 scale
+  // bytes of its blocks, which sit in scale tile 2t + g/2 at byte offset 4 (g % 2).
+  // The next super tile's operands are in flight while this one is multiplied.
+  struct Tile {
+    uint4 bc[4][2];
+    uint32_t bs[4];
+    uint4 ac[MT][2];
+    uint32_t as[MT];
+  };
+  auto fetch = [&](int64_t st, Tile& T) {
+    const int64_t off = st * 128 + 32 * g;           // code byte offset of this lane's 32 bytes
+    const int64_t kt = 2 * st + (g >> 1);             // its scale tile
+    const bool c0 = off < half_k, c1 = off + 16 < half_k, sv = kt < kt_all;   // partial last super tile
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      T.bc[j][0] = c0 ? *reinterpret_cast<const uint4*>(brow[j] + off) : make_uint4(0, 0, 0, 0);
+      T.bc[j][1] = c1 ? *reinterpret_cast<const uint4*>(brow[j] + off + 16) : make_uint4(0, 0, 0, 0);
+      T.bs[j] = sv ? *reinterpret_cast<const uint32_t*>(bsrow[j] + kt * n * 8) : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      T.ac[i][0] = c0 ? *reinterpret_cast<const uint4*>(arow[i] + off) : make_uint4(0, 0, 0, 0);
+      T.ac[i][1] = c1 ? *reinterpret_cast<const uint4*>(arow[i] + off + 16) : make_uint4(0, 0, 0, 0);
+      T.as[i] = sv ? *reinterpret_cast<const uint32_t*>(asrow[i] + kt * m * 8) : 0u;
+    }
+  };
+  auto multiply = [&](const Tile& T) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {                     // K values [64g + 8s, +8): block s/2
+      half8_t fb[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb[j] = dequant8(word(T.bc[j][s >> 2], s & 3), scale_pair(T.bs[j], s >> 1));
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        const half8_t fa = dequant8(word(T.ac[i][s >> 2], s & 3), scale_pair(T.as[i], s >> 1));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fb[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+  int64_t st = st_begin + wave;
+  if (st < st_end) {
+    Tile cur;
+    fetch(st, cur);
+    for (; st < st_end; st += kWaves) {
+      Tile nxt;
+      if (st + kWaves < st_end) fetch(st + kWaves, nxt);
+      multiply(cur);
+      cur = nxt;
+    }
+  }
+
+  // Sum the four waves' K subsets in wave order: ((w0 + w1) + w2) + w3.
+  for (int w = 1; w < kWaves; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) red[i * 4 + j][e][lane] = acc[i][j][e];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][e] += red[i * 4 + j][e][lane];
+    }
+    __syncthreads();
+  }
+  if (wave != 0) return;
+
+  // 16x16 MFMA output: lane holds column l16 of each tile, rows 4g .. 4g+3.
+  const float alpha = __fdiv_rn(1.0f, __fmul_rn(*gsf_a, *gsf_b));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t col = n0 + 16 * j + l16;
+    if (col >= n) continue;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t row = 16 * i + 4 * g + e;
+        if (row >= m) continue;
+        if (splits > 1) {
+          partial[((int64_t)split * m + row) * n + col] = acc[i][j][e];
+        } else {
+          uint32_t y = f32_to_bf16(__fmul_rn(alpha, __fmul_rn(acc[i][j][e], kAccUnscale)));
+          if (bias != nullptr) y = add_bias_bf16(y, bias[col]);
+          out[row * n + col] = (uint16_t)y;
+        }
+      }
+    }
+  }
+}
+
+// Sums the per-split partials [splits][m][n] in split order, then the epilogue.
+__global__ void __launch_bounds__(256) gemm_skinny_reduce(const float* __restrict__ partial, int splits, int64_t m,
+                                                          int64_t n, const float* __restrict__ gsf_a,
+                                                          const float* __restrict__ gsf_b,
+                                                          const uint16_t* __restrict__ bias, uint16_t* __restrict__ out) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= m * n) return;
+  float acc = 0.0f;
+  for (int sp = 0; sp < splits; ++sp) acc += partial[sp * m * n + idx];
+  const float alpha = __fdiv_rn(1.0f, __fmul_rn(*gsf_a, *gsf_b));
+  uint32_t y = f32_to_bf16(__fmul_rn(alpha, __fmul_rn(acc, kAccUnscale)));
+  if (bias != nullptr) y = add_bias_bf16(y, bias[idx % n]);
+  out[idx] = (uint16_t)y;
+}
+
+// Block-level K splits: enough blocks for about two per compute unit, each block keeping
+// at least one 256-wide super tile per wave.
+int skinny_splits(int64_t k, int64_t n, int cus) {
+  const int64_t groups = (n + kCols - 1) / kCols;
+  const int64_t st = ((k + BK - 1) / BK + 1) / 2;
+  int64_t sp = (2 * cus + groups - 1) / groups;
+  const int64_t max_sp = st / kWaves > 0 ? st / kWaves : 1;
+  if (sp > max_sp) sp = max_sp;
+  return (int)(sp < 1 ? 1 : sp);
+}
+
+template <int MT>
+hipError_t launch_mt(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, int64_t k, const uint8_t* b_codes,
+                     const uint8_t* b_scales, int64_t n, const float* gsf_a, const float* gsf_b, const uint16_t* bias,
+                     uint16_t* out, int splits, float* partial, hipStream_t s) {
+  const int64_t groups = (n + kCols - 1) / kCols;
+  hipLaunchKernelGGL(gemm_skinny_kernel<MT>, dim3((uint32_t)(groups * splits)), dim3(256), 0, s, a_codes, a_scales,
+                     m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, out, splits, partial);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool gemm_skinny_supported(int64_t m, int64_t k, const void* a_codes, const void* a_scales, const void* b_codes,
+                           const void* b_scales) {
+  return m <= 128 && (k / 2) % 16 == 0 && (((uintptr_t)a_codes | (uintptr_t)b_codes) & 15) == 0 &&
+         (((uintptr_t)a_scales | (uintptr_t)b_scales) & 3) == 0;
+}
+
+size_t gemm_skinny_workspace_bytes(int64_t m, int64_t k, int64_t n, int cus) {
+  const int sp = skinny_splits(k, n, cus);
+  return sp > 1 ? (size_t)sp * (size_t)m * (size_t)n * sizeof(float) : 0;
+}
+
+hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, int64_t k,
+                              const uint8_t* b_codes, const uint8_t* b_scales, int64_t n, const float* gsf_a,
+                              const float* gsf_b, const uint16_t* bias, uint16_t* out, void* workspace,
+                              size_t workspace_bytes, int cus, hipStream_t s) {
+  int splits = skinny_splits(k, n, cus);
+  const size_t need = splits > 1 ? (size_t)splits * (size_t)m * (size_t)n * sizeof(float) : 0;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) splits = 1;
+  float* partial = splits > 1 ? static_cast<float*>(workspace) : nullptr;
+  hipError_t e;
+  if (m <= 16) e = launch_mt<1>(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, out, splits, partial, s);
+  else if (m <= 32) e = launch_mt<2>(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, out, splits, partial, s);
+  else if (m <= 64) e = launch_mt<4>(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, out, splits, partial, s);
+  else e = launch_mt<8>(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, out, splits, partial, s);
+  if (e != hipSuccess || splits == 1) return e;
+  const int64_t total = m * n;
+  hipLaunchKernelGGL(gemm_skinny_reduce, dim3((uint32_t)((total + 255) / 256)), dim3(256), 0, s, partial, splits, m,
+                     n, gsf_a, gsf_b, bias, out);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -32,8 +32,8 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t 
 // Compute units of the current device (cached per device).
 int compute_units();
 
-// The software-pipelined 256 x 256-tile GEMM (gemm_pipe.hip): used for M >= 512 when K
-// is a multiple of 32 and every operand pointer is 16-byte aligned.  Tiles beyond the
+// The software-pipelined 256 x 256-tile GEMM (gemm_pipe.hip): K a multiple of 32 and
+// every operand pointer 16-byte aligned.  Tiles beyond the
 // last whole round (one tile per compute unit) are split along K when the workspace
 // (gemm_pipe_workspace_bytes) allows; without it they run unsplit.
 bool gemm_pipe_supported(int64_t m, int64_t k, int64_t n, const void* a_codes, const void* a_scales,
@@ -43,6 +43,17 @@ hipError_t launch_gemm_pipe(const uint8_t* a_codes, const uint8_t* a_scales, int
                             const uint8_t* b_codes, const uint8_t* b_scales, int64_t n, const float* gsf_a,
                             const float* gsf_b, const uint16_t* bias, uint16_t* out, void* workspace,
                             size_t workspace_bytes, int cus, hipStream_t s);
+
+// The weight-streaming GEMM for m <= 128 (gemm_skinny.hip): K a multiple of 32, code
+// pointers 16-byte and scale pointers 4-byte aligned.  Splits K across blocks when the
+// workspace (gemm_skinny_workspace_bytes) allows.
+bool gemm_skinny_supported(int64_t m, int64_t k, const void* a_codes, const void* a_scales, const void* b_codes,
+                           const void* b_scales);
+size_t gemm_skinny_workspace_bytes(int64_t m, int64_t k, int64_t n, int cus);
+hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, int64_t k,
+                              const uint8_t* b_codes, const uint8_t* b_scales, int64_t n, const float* gsf_a,
+                              const float* gsf_b, const uint16_t* bias, uint16_t* out, void* workspace,
+                              size_t workspace_bytes, int cus, hipStream_t s);
 
 // Workspace the GEMM dispatcher can use for an [m, k] x [n, k] product (0 if none).
 size_t gemm_workspace_bytes(int64_t m, int64_t k, int64_t n);

@@ -98,9 +98,11 @@ __global__ void __launch_bounds__(kThreads) amax_partial_kernel(const uint16_t* 
 // Pass 2: quantize.  Eight consecutive lanes own one 128-wide K tile of one row
 // (a "unit"; lane j of the eight owns the 16-block j of the tile), so each group of
 // eight reads 256 contiguous bytes and writes 64 contiguous code bytes and the 8
-// scale bytes that are contiguous in the k-tile-major scale layout.  A block takes
-// kQuantUnits rounds of 32 units and loads all of them before computing.
-constexpr int kQuantUnits = 4;
+// scale bytes that are contiguous in the k-tile-major scale layout.  Blocks take the
+// global scale once, then loop over groups of kQuantUnits x 32 units, loading a
+// group's units before computing them.
+constexpr int kQuantUnits = 2;
+constexpr int kQuantBlocks = 2048;   // grid cap: blocks loop over the units
 
 template <bool kRotate>
 __global__ void __launch_bounds__(kThreads) quantize_kernel(
@@ -111,22 +113,6 @@ __global__ void __launch_bounds__(kThreads) quantize_kernel(
   const int64_t kt_count = (k + kScaleTileK - 1) / kScaleTileK;
   const int64_t nb = k / kBlock;
   const int j = threadIdx.x & 7;
-
-  float v[kQuantUnits][16];
-  int64_t row[kQuantUnits], kt[kQuantUnits];
-#pragma unroll
-  for (int u = 0; u < kQuantUnits; ++u) {
-    const int64_t unit = ((int64_t)blockIdx.x * kQuantUnits + u) * (kThreads / 8) + (threadIdx.x >> 3);
-    row[u] = unit / kt_count;
-    kt[u] = unit - row[u] * kt_count;
-    const int64_t blk = kt[u] * 8 + j;
-    if (row[u] < m_rows && blk < nb) {
-      load16_bf16(x + row[u] * k + blk * kBlock, v[u]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v[u][i] = 0.0f;
-    }
-  }
 
   float gsf;
   if (static_gsf != nullptr) {
@@ -139,35 +125,55 @@ __global__ void __launch_bounds__(kThreads) quantize_kernel(
   }
   if (gsf_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *gsf_out = gsf;
 
+  const int64_t units_total = m_rows * kt_count;
+  const int64_t per_block = (int64_t)kQuantUnits * (kThreads / 8);
+  for (int64_t base = (int64_t)blockIdx.x; base * per_block < units_total; base += gridDim.x) {
+    float v[kQuantUnits][16];
+    int64_t row[kQuantUnits], kt[kQuantUnits];
 #pragma unroll
-  for (int u = 0; u < kQuantUnits; ++u) {
-    if (kRotate) rotate16_bf16(v[u], group, inv_sqrt_g);
-    const int64_t blk = kt[u] * 8 + j;
-    const bool in_row = row[u] < m_rows;
-    const bool valid = in_row && blk < nb;
-    float bmax = 0.0f;
+    for (int u = 0; u < kQuantUnits; ++u) {
+      const int64_t unit = (base * kQuantUnits + u) * (kThreads / 8) + (threadIdx.x >> 3);
+      row[u] = unit / kt_count;
+      kt[u] = unit - row[u] * kt_count;
+      const int64_t blk = kt[u] * 8 + j;
+      if (row[u] < m_rows && blk < nb) {
+        load16_bf16(x + row[u] * k + blk * kBlock, v[u]);
+      } else {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) bmax = fmaxf(bmax, fabsf(v[u][i]));
-    const uint32_t s8 = valid ? block_scale_byte(gsf, bmax) : 0u;
-    uint32_t w0 = 0, w1 = 0;
-    if (s8 != 0) {
-      const float r = __fdiv_rn(gsf, e4m3_decode(s8));
-      float p[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) p[i] = __fmul_rn(v[u][i], r);
-      w0 = e2m1_encode8(p);
-      w1 = e2m1_encode8(p + 8);
+        for (int i = 0; i < 16; ++i) v[u][i] = 0.0f;
+      }
     }
-    if (valid) *reinterpret_cast<uint2*>(codes + row[u] * (k / 2) + blk * 8) = make_uint2(w0, w1);
-    // gather the unit's 8 scale bytes into lane j == 0 and write them as one 8-byte word
-    uint32_t lo = j < 4 ? s8 << (8 * j) : 0u;
-    uint32_t hi = j >= 4 ? s8 << (8 * (j - 4)) : 0u;
+
 #pragma unroll
-    for (int o = 1; o < 8; o <<= 1) {
-      lo |= __shfl_xor(lo, o, 64);
-      hi |= __shfl_xor(hi, o, 64);
+    for (int u = 0; u < kQuantUnits; ++u) {
+      if (kRotate) rotate16_bf16(v[u], group, inv_sqrt_g);
+      const int64_t blk = kt[u] * 8 + j;
+      const bool in_row = row[u] < m_rows;
+      const bool valid = in_row && blk < nb;
+      float bmax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) bmax = fmaxf(bmax, fabsf(v[u][i]));
+      const uint32_t s8 = valid ? block_scale_byte(gsf, bmax) : 0u;
+      uint32_t w0 = 0, w1 = 0;
+      if (s8 != 0) {
+        const float r = __fdiv_rn(gsf, e4m3_decode(s8));
+        float p[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) p[i] = __fmul_rn(v[u][i], r);
+        w0 = e2m1_encode8(p);
+        w1 = e2m1_encode8(p + 8);
+      }
+      if (valid) *reinterpret_cast<uint2*>(codes + row[u] * (k / 2) + blk * 8) = make_uint2(w0, w1);
+      // gather the unit's 8 scale bytes into lane j == 0 and write them as one 8-byte word
+      uint32_t lo = j < 4 ? s8 << (8 * j) : 0u;
+      uint32_t hi = j >= 4 ? s8 << (8 * (j - 4)) : 0u;
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) {
+        lo |= __shfl_xor(lo, o, 64);
+        hi |= __shfl_xor(hi, o, 64);
+      }
+      if (j == 0 && in_row) *reinterpret_cast<uint2*>(scales + (kt[u] * m_rows + row[u]) * 8) = make_uint2(lo, hi);
     }
-    if (j == 0 && in_row) *reinterpret_cast<uint2*>(scales + (kt[u] * m_rows + row[u]) * 8) = make_uint2(lo, hi);
   }
 }
 
@@ -255,7 +261,8 @@ hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t k, int group
   const int64_t kt_count = (k + kScaleTileK - 1) / kScaleTileK;
   const int64_t units = rows * kt_count;
   const int64_t per_block = (int64_t)kQuantUnits * (kThreads / 8);
-  const int64_t grid = (units + per_block - 1) / per_block;
+  int64_t grid = (units + per_block - 1) / per_block;
+  if (grid > kQuantBlocks) grid = kQuantBlocks;
   if (group > 1)
     hipLaunchKernelGGL(quantize_kernel<true>, dim3((uint32_t)grid), dim3(kThreads), 0, s, x, rows, k, group, inv_sqrt_g,
                        static_gsf, partials, n_partials, codes, scales, gsf_out);

@@ -43,7 +43,12 @@ def test_sizes():
     # 64 tiles of 256x256 on 256 CUs split four ways: 4 * 64 fp32 tiles of partials
     assert L.nvfp4_gemm_workspace_bytes(4096, 5120, 1024) == 4 * 64 * 65536 * 4
     assert L.nvfp4_gemm_workspace_bytes(4096, 5120, 16384) == 0      # whole rounds only
-    assert L.nvfp4_gemm_workspace_bytes(100, 5120, 1024) == 0        # small M: no split
+    # few rows: 16 column groups of 64, K split 5 ways (20 super tiles of 256, >= 4 per block)
+    assert L.nvfp4_gemm_workspace_bytes(100, 5120, 1024) == 5 * 100 * 1024 * 4
+    # mid M: 8 tiles of 256x256, split 20 ways (40 K tiles, >= 2 per split)
+    assert L.nvfp4_gemm_workspace_bytes(300, 5120, 1024) == 20 * 8 * 65536 * 4
+    # never more partials than one tile per compute unit
+    assert L.nvfp4_gemm_workspace_bytes(128, 25600, 5120) <= 256 * 65536 * 4
 
 
 def _msg():

@@ -179,3 +179,47 @@ def test_probe_near_the_pages_figure():
     out_bad = nv().nvfp4_linear(x.to(DEV), packed, bad, gsf_w, None, 1024)
     err_bad = o.probe_relative_error(out_bad.float().cpu().numpy(), x.float().numpy(), w.float().numpy())
     assert err_bad > 2.5 * err
+
+
+@pytest.mark.parametrize("m", [1, 5, 16, 17, 40, 64, 100, 128])
+@pytest.mark.parametrize("n,k", [(1024, 5120), (300, 4128), (5120, 1024)])
+def test_few_rows_weight_streaming(m, n, k):
+    """Decode shapes (M <= 128): the weight-streaming kernel, with and without the
+    block-level K split, against the oracle; ragged N and a partial last K tile."""
+    rng = np.random.default_rng(m * 7 + n + k)
+    px, sx = random_operands(rng, m, k)
+    pw, sw = random_operands(rng, n, k)
+    bias = workloads.draw("normal", (n,), 6, n)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    args = (t(px), t(canonical_to_layout(sx, k)), t(pw), t(canonical_to_layout(sw, k)), 1.5, 0.25, bias.to(DEV))
+    split = nv().nvfp4_gemm(*args)
+    again = nv().nvfp4_gemm(*args)
+    whole = nv().nvfp4_gemm(*args, split_k=False)
+    torch.cuda.synchronize()
+    assert torch.equal(split, again)
+    alpha = o.alpha_of(1.5, 0.25)
+    ref = o.nvfp4_gemm(px, sx, pw, sw, alpha, bias.float().numpy())
+    bound = accumulation_bound(o.dequantize(px, sx), o.dequantize(pw, sw), alpha)
+    assert_gemm_close(split.float().cpu().numpy(), ref, bound)
+    assert_gemm_close(whole.float().cpu().numpy(), ref, bound)
+
+
+@pytest.mark.parametrize("m,n,k", [(65, 4352, 1056), (200, 4100, 2080), (511, 1000, 640), (128, 25600, 512)])
+def test_mid_rows_pipelined_split(m, n, k):
+    """Between the decode and the full-tile shapes: the pipelined kernel on a single
+    row of ragged 256x256 tiles, split along K up to one tile per compute unit."""
+    rng = np.random.default_rng(m + 3 * n + k)
+    px, sx = random_operands(rng, m, k)
+    pw, sw = random_operands(rng, n, k)
+    bias = workloads.draw("normal", (n,), 7, n)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    args = (t(px), t(canonical_to_layout(sx, k)), t(pw), t(canonical_to_layout(sw, k)), 0.5, 3.0, bias.to(DEV))
+    a = nv().nvfp4_gemm(*args)
+    b = nv().nvfp4_gemm(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    cols = np.unique(np.concatenate([np.arange(n - 20, n), rng.choice(n, 400)]))
+    alpha = o.alpha_of(0.5, 3.0)
+    ref = o.nvfp4_gemm(px, sx, pw[cols], sw[cols], alpha, bias.float().numpy()[cols])
+    bound = accumulation_bound(o.dequantize(px, sx), o.dequantize(pw[cols], sw[cols]), alpha)
+    assert_gemm_close(a.float().cpu().numpy()[:, cols], ref, bound)
