@@ -30,14 +30,109 @@ QUANT_BYTES_PER_ELEM = 2.0 + 0.5625           # quantize pass: bf16 read, codes 
 AMAX_QUANT_BYTES_PER_ELEM = 2.0 + QUANT_BYTES_PER_ELEM
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_gate_4096x5120x25600.txt")
+COPY_BYTES = 1 << 30          # the calibration copy: 1 GiB read, 1 GiB written
+
+
 def parse():
     p = argparse.ArgumentParser(description=__doc__)
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
-    p.add_argument("--cpu-rows", type=int, default=1024, help="rows of the CPU oracle sample")
+    p.add_argument("--cpu-rows", type=int, default=M, help="rows of the CPU oracle sample")
+    p.add_argument("--part", choices=("step", "gemm", "quantize", "copy"),
+                   help="run only this part (warmup + steps launches, no JSON line): for counter runs")
+    p.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                   help="summarise rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of --part step and --part copy")
     return p.parse_args()
+
+
+def kernel_source_digest() -> str:
+    """Digest of the kernel sources: counter figures taken on other sources are stale."""
+    import hashlib
+    d = os.path.join(ROOT, "nvfp4_w4a4_quantized_global_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def _pmc_rows(directory: str, counter: str) -> dict:
+    """Median value of `counter` per dispatch, by kernel name, from rocprofv3 csv output
+    (the median keeps a first, cold dispatch from skewing the figure)."""
+    import csv
+    import glob
+    sums = {}
+    files = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {directory}")
+    for path in files:
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                name = row["Kernel_Name"]
+                key = (name, row.get("Dispatch_Id", row.get("Correlation_Id", "")))
+                sums[key] = sums.get(key, 0.0) + float(row["Counter_Value"])
+    per_kernel = {}
+    for (name, _), v in sums.items():
+        per_kernel.setdefault(name, []).append(v)
+    import statistics
+    return {k: (statistics.median(v), len(v)) for k, v in per_kernel.items()}
+
+
+def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir) -> None:
+    """Text summary of the counter runs: per kernel, FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) scaled to bytes by what the same counters read for a 1 GiB copy."""
+    fetch, write = _pmc_rows(fetch_dir, "FETCH_SIZE"), _pmc_rows(write_dir, "WRITE_SIZE")
+    cf, cw = _pmc_rows(copy_fetch_dir, "FETCH_SIZE"), _pmc_rows(copy_write_dir, "WRITE_SIZE")
+    print(f"source_digest: {kernel_source_digest()}")
+    # the scale comes from the elementwise copy (the access pattern of the library's
+    # kernels); the runtime copy kernel's figures are listed beside it
+    copies = [k for k in cf if "Mul" in k and cf[k][0] > 0] + [k for k in cf if "copyBuffer" in k]
+    for i, name in enumerate(copies):
+        tag = "copy" if i == 0 else f"copy_alt{i}"
+        print(f"{tag}_kernel: {name}")
+        print(f"{tag}_fetch_kib: {cf[name][0]:.1f}")
+        print(f"{tag}_write_kib: {cw[name][0]:.1f}")
+        print(f"{tag}_fetch_scale: {COPY_BYTES / (cf[name][0] * 1024.0):.4f}")
+        print(f"{tag}_write_scale: {COPY_BYTES / (cw[name][0] * 1024.0):.4f}")
+    f_scale = COPY_BYTES / (cf[copies[0]][0] * 1024.0)
+    w_scale = COPY_BYTES / (cw[copies[0]][0] * 1024.0)
+    print("# kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled read MB | scaled write MB")
+    for name in sorted(fetch, key=lambda k: -fetch[k][0]):
+        fk, nd = fetch[name]
+        wk = write.get(name, (0.0, 0))[0]
+        print(f"kernel: {name} | {nd} | {fk:.1f} | {wk:.1f} | {fk * 1024 * f_scale / 1e6:.2f} | "
+              f"{wk * 1024 * w_scale / 1e6:.2f}")
+
+
+def read_traffic(kernel_names: tuple) -> float | None:
+    """HBM bytes per call of the kernels whose names contain one of kernel_names, from the
+    committed counter summary, or None if there is none or the kernels changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return None
+    kv = {}
+    total = 0.0
+    found = False
+    for line in lines:
+        if line.startswith("kernel: "):
+            name, _nd, fk, wk, rmb, wmb = [c.strip() for c in line[len("kernel: "):].split("|")]
+            if any(k in name for k in kernel_names):
+                total += (float(rmb) + float(wmb)) * 1e6
+                found = True
+        elif ": " in line and not line.startswith("#"):
+            a, b = line.split(": ", 1)
+            kv[a.strip()] = b.strip()
+    if not found or kv.get("source_digest") != kernel_source_digest():
+        return None
+    return total
 
 
 def time_on_stream(fn, iters: int, stream) -> float:
@@ -77,8 +172,15 @@ def cpu_baseline(x_cpu, w_cpu, rows: int) -> dict:
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+GEMM_KERNELS = ("::gemm_pipe_kernel<", "::split_k_reduce(")
+QUANT_KERNELS = ("::amax_partial_kernel<", "::quantize_kernel<")
+
+
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
               file=sys.stderr)
@@ -88,6 +190,19 @@ def main():
     import workloads
 
     dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    if args.part == "copy":
+        # two plain copies of 1 GiB: the runtime's copy kernel, and torch's vectorised
+        # elementwise kernel (16-byte loads and stores per lane, like the library's kernels)
+        src = torch.empty((COPY_BYTES // 2,), dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print(f"copy: 2 x {args.warmup + args.steps} x {COPY_BYTES} bytes", flush=True)
+        return
+
     lin = workloads.headline_gate()
     x = lin.x.to(dev)
     w = lin.w.to(dev)
@@ -95,10 +210,25 @@ def main():
     del w
     ws = torch.empty((nv.linear_workspace_bytes(M, K, N),), dtype=torch.uint8, device=dev)
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    stream = torch.cuda.current_stream(dev)
+    codes, scales, gsf_x = nv.quantize_activation(x)
+    gws = torch.empty((max(nv.gemm_workspace_bytes(M, K, N), 1),), dtype=torch.uint8, device=dev)
 
     def step():
         nv.nvfp4_linear(x, packed, inv_scale, gsf_w, None, N, None, 0, ws, out)
+
+    def quant():
+        nv.quantize_activation(x)
+
+    def gemm():
+        nv.nvfp4_gemm(codes, scales, packed, inv_scale, gsf_x, gsf_w, None, out, gws)
+
+    if args.part is not None:
+        fn = {"step": step, "gemm": gemm, "quantize": quant}[args.part]
+        for _ in range(args.warmup + args.steps):
+            fn()
+        torch.cuda.synchronize()
+        print(f"{args.part}: {args.warmup + args.steps} calls", flush=True)
+        return
 
     for _ in range(args.warmup):
         step()
@@ -109,17 +239,7 @@ def main():
     wall = time.perf_counter() - t0
     tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
 
-    # quantize pass alone (amax + quantize, dynamic scale), and the GEMM kernel alone
-    codes, scales, gsf_x = nv.quantize_activation(x)
-
-    def quant():
-        nv.quantize_activation(x)
-
-    gws = torch.empty((max(nv.gemm_workspace_bytes(M, K, N), 1),), dtype=torch.uint8, device=dev)
-
-    def gemm():
-        nv.nvfp4_gemm(codes, scales, packed, inv_scale, gsf_x, gsf_w, None, out, gws)
-
+    # the quantize pass alone (amax + quantize, dynamic scale) and the GEMM alone
     for f in (quant, gemm):
         f()
     torch.cuda.synchronize()
@@ -128,6 +248,8 @@ def main():
     g_ms = time_on_stream(gemm, iters, stream)
     q_gbs = M * K * AMAX_QUANT_BYTES_PER_ELEM / (q_ms * 1e-3) / 1e9
     g_tflops = 2.0 * M * N * K / (g_ms * 1e-3) / 1e12
+    g_traffic = read_traffic(GEMM_KERNELS)
+    q_traffic = read_traffic(QUANT_KERNELS)
 
     rec = {
         "metric": "NVFP4 linear TFLOP/s (quant+GEMM) at M=4096,K=5120,N=25600; quantize GB/s",
@@ -148,9 +270,14 @@ def main():
         "quantize_gbs": round(q_gbs, 1),
         "quantize_ms": round(q_ms, 4),
         "quantize_hbm_frac": round(q_gbs / PEAK_HBM_GBS, 4),
-        "roofline": {"kernel": "gemm_kernel (nvfp4 block-scaled GEMM)", "bound": "mfma",
+        "quantize_traffic": None if q_traffic is None else round(q_traffic),
+        "roofline": {"kernel": "nvfp4_gemm: gemm_pipe_kernel<false> (1536 whole 256x256 tiles) + "
+                               "gemm_pipe_kernel<true> (64 tiles x 4 K splits) + split_k_reduce",
+                     "bound": "mfma",
                      "achieved": round(g_tflops, 2), "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(g_tflops / PEAK_F16_MFMA_TFLOPS, 4), "traffic": None,
+                     "frac": round(g_tflops / PEAK_F16_MFMA_TFLOPS, 4),
+                     "traffic": None if g_traffic is None else round(g_traffic),
+                     "algorithmic_bytes": round(M * K * 0.5625 + N * K * 0.5625 + M * N * 2),
                      "frac_of_fp4_peak": round(g_tflops / PEAK_FP4_MFMA_TFLOPS, 4),
                      "avg_launch_us": round(g_ms * 1e3, 2)},
         "wall_s_timed": round(wall, 3),

@@ -68,6 +68,9 @@ __device__ __forceinline__ void interleave16() {
   __builtin_amdgcn_sched_barrier(0);   // nothing crosses a sub-step boundary
 }
 
+// kSplit: the launch for the tiles past the last whole round, each split along K into
+// fp32 partials (`splits` blocks per tile); otherwise whole tiles with the epilogue.
+template <bool kSplit>
 __global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m, int64_t k,
     const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, int64_t n,
@@ -81,7 +84,7 @@ __global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
   const int nblk = gridDim.x;
   int bid = blockIdx.x;
   int split = 0;
-  if (splits > 1) {
+  if (kSplit) {
     split = bid % splits;
     bid = bid / splits;
   } else if ((nblk & 7) == 0) {
@@ -101,8 +104,9 @@ __global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
   const int kh = lane >> 5;
   const int64_t half_k = k / 2;
   const int64_t kt_all = (k + BK - 1) / BK;
-  const int64_t kt_begin = kt_all * split / splits;        // this block's K tiles
-  const int64_t kt_end = kt_all * (split + 1) / splits;
+  const int nsplit = kSplit ? splits : 1;
+  const int64_t kt_begin = kt_all * split / nsplit;        // this block's K tiles
+  const int64_t kt_end = kt_all * (split + 1) / nsplit;
 
   // Direct loads: wave w, instruction i fills LDS rows 16*(4w+i) .. +15 of an operand;
   // lane l lands in slot (l & 3) of row 16*(4w+i) + l/4 and so fetches logical chunk
@@ -260,7 +264,7 @@ __global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
   }
   stage_barrier();   // no load still landing in LDS, every wave done with the stages
 
-  if (splits > 1) {
+  if (kSplit) {
     // Split-K: the raw fp32 accumulators of this K range, in register order (entry q of
     // thread t at ((split * tiles + tile) * 256 + q) * 256 + t); split_k_reduce finishes.
     const int tiles = gridDim.x / splits;
@@ -396,8 +400,11 @@ hipError_t launch_gemm_pipe(const uint8_t* a_codes, const uint8_t* a_scales, int
                             size_t workspace_bytes, int cus, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_pipe_kernel),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_pipe_kernel<false>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_pipe_kernel<true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
@@ -406,18 +413,23 @@ hipError_t launch_gemm_pipe(const uint8_t* a_codes, const uint8_t* a_scales, int
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) p.splits = 1;
   const int tm = (int)p.tiles_m, tn = (int)p.tiles_n;
   if (p.full > 0) {
-    hipLaunchKernelGGL(gemm_pipe_kernel, dim3((uint32_t)p.full), dim3(256), kLds, s, a_codes, a_scales, m, k, b_codes,
+    hipLaunchKernelGGL(gemm_pipe_kernel<false>, dim3((uint32_t)p.full), dim3(256), kLds, s, a_codes, a_scales, m, k, b_codes,
                        b_scales, n, gsf_a, gsf_b, bias, out, n, n, tm, tn, 0, 1, (float*)nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (p.rest == 0) return hipSuccess;
   float* partial = static_cast<float*>(workspace);
-  hipLaunchKernelGGL(gemm_pipe_kernel, dim3((uint32_t)(p.rest * p.splits)), dim3(256), kLds, s, a_codes, a_scales, m, k,
-                     b_codes, b_scales, n, gsf_a, gsf_b, bias, out, n, n, tm, tn, (int)p.full, p.splits,
-                     p.splits > 1 ? partial : (float*)nullptr);
+  if (p.splits == 1) {
+    hipLaunchKernelGGL(gemm_pipe_kernel<false>, dim3((uint32_t)p.rest), dim3(256), kLds, s, a_codes, a_scales, m, k,
+                       b_codes, b_scales, n, gsf_a, gsf_b, bias, out, n, n, tm, tn, (int)p.full, 1, (float*)nullptr);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(gemm_pipe_kernel<true>, dim3((uint32_t)(p.rest * p.splits)), dim3(256), kLds, s, a_codes,
+                     a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, out, n, n, tm, tn, (int)p.full,
+                     p.splits, partial);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.splits == 1) return e;
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(split_k_reduce, dim3((uint32_t)(p.rest * 256)), dim3(256), 0, s, partial, p.splits, (int)p.rest,
                      (int)p.full, tm, m, n, gsf_a, gsf_b, bias, out, n);
   return hipGetLastError();

@@ -81,8 +81,11 @@ def test_split_k_tail(m, n, k):
     a = nv().nvfp4_gemm(*args)
     b = nv().nvfp4_gemm(*args)
     c = nv().nvfp4_gemm(*args, split_k=False)
+    # a workspace full of garbage: every partial is written before it is read
+    ws = torch.full((nv().gemm_workspace_bytes(m, k, n),), 0x7F, dtype=torch.uint8, device=DEV)
+    d = nv().nvfp4_gemm(*args, workspace=ws)
     torch.cuda.synchronize()
-    assert torch.equal(a, b)
+    assert torch.equal(a, b) and torch.equal(a, d)
     got = a.float().cpu().numpy()
     rows = np.unique(np.concatenate([np.arange(m - 8, m), rng.choice(m, 120)]))
     alpha = o.alpha_of(2.0, 0.5)
