@@ -136,3 +136,41 @@ def test_binding_rejects_bad_arguments():
         nv().NVFP4Linear(packed, inv_scale, gsf_w, None, lin.k, None, "bogus")
     with pytest.raises(ValueError):
         nv().NVFP4Linear.from_weight(torch.zeros((8, 24), device=DEV, dtype=torch.bfloat16))
+
+
+_DECODE_WEIGHTS = {}
+
+
+def _decode_weight(name):
+    """GPU-quantized decode-sweep weight (quantized once per projection)."""
+    if name not in _DECODE_WEIGHTS:
+        w = workloads.small_m_weight(name)
+        packed, inv_scale, gsf_w = nv().quantize_weight(w.to(DEV))
+        _DECODE_WEIGHTS.clear()            # keep one projection's weight resident at a time
+        _DECODE_WEIGHTS[name] = (w, packed, inv_scale, gsf_w)
+    return _DECODE_WEIGHTS[name]
+
+
+@pytest.mark.parametrize("m", [1, 16, 128])
+@pytest.mark.parametrize("name", [p[0] for p in workloads.QWEN3_PROJECTIONS])
+def test_decode_sweep_sampled_columns(name, m):
+    """The small-M sweep through nvfp4_linear in the launch configuration the decode
+    benchmark uses: every output row, on 160 sampled output columns (plus the last 16),
+    against the oracle; the sampled weight rows' codes and scales must be bit-exact."""
+    print(f"[decode sweep] M={m} {name}", flush=True)
+    w, packed, inv_scale, gsf_w = _decode_weight(name)
+    n, k = w.shape
+    x = workloads.small_m_input(m, name)
+    out = nv().nvfp4_linear(x.to(DEV), packed, inv_scale, gsf_w, None, n)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(m * 100 + n)
+    cols = np.unique(np.concatenate([rng.choice(n, 160, replace=False), np.arange(n - 16, n)]))
+    wf = w.float().numpy()
+    gw = o.global_sf(o.amax(wf))
+    assert np.float32(gsf_w.item()) == gw
+    nib, sw = o.nvfp4_quantize(wf[cols], gw)
+    pw = o.pack_codes(nib)
+    assert np.array_equal(packed[torch.from_numpy(cols).to(DEV)].cpu().numpy(), pw)
+    r = o.nvfp4_linear_inference(x.float().numpy(), pw, sw, gw, None)
+    bound = accumulation_bound(o.dequantize(r["codes"], r["scales"]), o.dequantize(pw, sw), r["alpha"])
+    assert_gemm_close(out.float().cpu().numpy()[:, cols], r["out"], bound)

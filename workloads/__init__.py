@@ -37,7 +37,7 @@ import torch
 
 __all__ = [
     "Linear", "draw", "tiny_linear", "qwen3_attention", "qwen3_mlp", "vit_decoder_tiles",
-    "small_m_sweep", "QWEN3_PROJECTIONS", "VIT_LINEARS", "headline_gate",
+    "small_m_sweep", "small_m_weight", "small_m_input", "QWEN3_PROJECTIONS", "VIT_LINEARS", "headline_gate",
 ]
 
 # (name, out_features N, in_features K) of one Qwen3-32B-shaped decoder layer.
@@ -179,12 +179,25 @@ def vit_decoder_tiles(seed: int = 3, tiles: int = 8, tokens: int = 4096, group_s
     return out
 
 
+def small_m_weight(name: str, seed: int = 4):
+    """The decode sweep's weight for one projection, W N(0,0.02) bf16 [N, K]."""
+    i = [p[0] for p in QWEN3_PROJECTIONS].index(name)
+    _, n, k = QWEN3_PROJECTIONS[i]
+    return draw("normal", (n, k), seed, 100 + i, 0.02)
+
+
+def small_m_input(m: int, name: str, seed: int = 4, ms: tuple[int, ...] = (1, 16, 128)):
+    """The decode sweep's activation for one (M, projection) pair, x N(0,1) bf16 [M, K]."""
+    i = [p[0] for p in QWEN3_PROJECTIONS].index(name)
+    j = ms.index(m)
+    return draw("normal", (m, QWEN3_PROJECTIONS[i][2]), seed, 1000 * (j + 1) + i)
+
+
 def small_m_sweep(seed: int = 4, ms: tuple[int, ...] = (1, 16, 128)) -> list[Linear]:
     """Every (M, projection) pair of the decode sweep; x N(0,1), W N(0,0.02)."""
-    weights = {name: draw("normal", (n, k), seed, 100 + i, 0.02) for i, (name, n, k) in enumerate(QWEN3_PROJECTIONS)}
+    weights = {name: small_m_weight(name, seed) for name, _, _ in QWEN3_PROJECTIONS}
     out = []
-    for j, m in enumerate(ms):
-        for i, (name, n, k) in enumerate(QWEN3_PROJECTIONS):
-            x = draw("normal", (m, k), seed, 1000 * (j + 1) + i)
-            out.append(Linear(f"M{m}.{name}", x, weights[name], meta={"m": m}))
+    for m in ms:
+        for name, _, _ in QWEN3_PROJECTIONS:
+            out.append(Linear(f"M{m}.{name}", small_m_input(m, name, seed, ms), weights[name], meta={"m": m}))
     return out
