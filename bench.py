@@ -38,7 +38,9 @@ def parse():
     p = argparse.ArgumentParser(description=__doc__)
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=5)
+    # ~30 ms of untimed steps: the first tens of ms of load after an idle host-side
+    # set-up run measurably slower while the chip's clocks ramp up
+    p.add_argument("--warmup", type=int, default=30)
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
     p.add_argument("--cpu-rows", type=int, default=M, help="rows of the CPU oracle sample")
     p.add_argument("--part", choices=("step", "gemm", "quantize", "copy"),
