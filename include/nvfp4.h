@@ -74,6 +74,11 @@ size_t nvfp4_quantize_workspace_bytes(void);
  * the compute-unit count of the current device. */
 size_t nvfp4_linear_workspace_bytes(int64_t m, int64_t k, int64_t n);
 
+/* Workspace nvfp4_linear_segmented needs for `segments` row blocks of seg_rows rows:
+ * the nvfp4_linear workspace of the whole [segments * seg_rows, k] input with one
+ * global-scale slot per segment.  0 for segments outside [1, 1024]. */
+size_t nvfp4_linear_segmented_workspace_bytes(int64_t segments, int64_t seg_rows, int64_t k, int64_t n);
+
 /* Workspace nvfp4_gemm can use for an [m, k] x [n, k] product (fp32 partial sums of
  * output tiles split along K to fill the GPU); 0 when the product would not split.
  * Depends on the compute-unit count of the current device. */
@@ -116,6 +121,19 @@ int nvfp4_quantize_activation(const void* x_dev, int64_t m, int64_t k,
                               void* workspace_dev, size_t workspace_bytes, void* stream);
 
 /*
+ * nvfp4_quantize_activation_segmented: nvfp4_quantize_activation with a dynamic scale
+ * applied separately to `segments` consecutive row blocks of seg_rows rows each, as
+ * `segments` separate calls would ([TILES]: a dynamic-scale decoder takes one global
+ * scale per tile).  x_dev bf16 [segments * seg_rows][k]; codes_dev / scale_dev as for
+ * the whole input (scale layout with segments * seg_rows rows); gsf_out_dev receives
+ * `segments` fp32 scales.  segments: 1..1024.
+ */
+int nvfp4_quantize_activation_segmented(const void* x_dev, int64_t segments, int64_t seg_rows, int64_t k,
+                                        int rotation_group, uint8_t* codes_dev, uint8_t* scale_dev,
+                                        float* gsf_out_dev, void* workspace_dev, size_t workspace_bytes,
+                                        void* stream);
+
+/*
  * nvfp4_gemm: step 4 of [DEC] nvfp4_linear_inference (the mm_fp4 call and the bias
  * add).  out[i, j] = bf16(alpha * sum_b sx[i,b] sw[j,b] sum_{k in b} qx[i,k] qw[j,k]),
  * alpha = 1 / (gsf_x * gsf_w) in fp32; then, if bias_dev is not NULL,
@@ -149,6 +167,23 @@ int nvfp4_linear(const void* x_dev, int64_t m, int64_t k,
                  const float* global_sf_w_dev, const void* bias_dev, int64_t out_features,
                  const float* global_sf_x_dev, int rotation_group, void* out_dev,
                  void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/*
+ * nvfp4_linear_segmented: `segments` tiles of seg_rows rows through one linear in one
+ * pass, each tile with its own dynamic activation scale ([TILES]: batching the 8
+ * decoder tiles of a dynamic-scale NVFP4 decoder, which otherwise must decode one tile
+ * per call because a shared amax would change every tile's codes).  Row block s of
+ * out_dev equals nvfp4_linear on row block s of x_dev alone: the same codes, scales and
+ * global scale, the product up to fp32 summation order.  x_dev bf16
+ * [segments * seg_rows][k], out_dev bf16 [segments * seg_rows][out_features];
+ * gsf_out_dev: NULL or `segments` fp32 (the per-tile scales).  Other arguments as for
+ * nvfp4_linear; workspace >= nvfp4_linear_segmented_workspace_bytes.  segments: 1..1024.
+ */
+int nvfp4_linear_segmented(const void* x_dev, int64_t segments, int64_t seg_rows, int64_t k,
+                           const uint8_t* packed_dev, const uint8_t* inv_scale_dev,
+                           const float* global_sf_w_dev, const void* bias_dev, int64_t out_features,
+                           int rotation_group, void* out_dev, float* gsf_out_dev,
+                           void* workspace_dev, size_t workspace_bytes, void* stream);
 
 /* Scale-layout conversion: layout above <-> row-major [rows][k/16] bytes. */
 int nvfp4_scale_to_canonical(const uint8_t* layout_dev, uint8_t* canonical_dev,

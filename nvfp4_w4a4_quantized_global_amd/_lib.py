@@ -31,11 +31,15 @@ SIGNATURES = {
     "nvfp4_quantize_workspace_bytes": (_sz, []),
     "nvfp4_linear_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "nvfp4_gemm_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "nvfp4_linear_segmented_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
     "rotate_activation": (_int, [_vp, _int, _vp, _int, _i64, _i64, _int, _vp]),
     "nvfp4_quantize_weight": (_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_quantize_activation": (_int, [_vp, _i64, _i64, _vp, _int, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "nvfp4_quantize_activation_segmented": (_int, [_vp, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_gemm": (_int, [_vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_linear": (_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _int, _vp, _vp, _sz, _vp]),
+    "nvfp4_linear_segmented": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _int, _vp, _vp, _vp, _sz,
+                                      _vp]),
     "nvfp4_scale_to_canonical": (_int, [_vp, _vp, _i64, _i64, _vp]),
     "nvfp4_scale_from_canonical": (_int, [_vp, _vp, _i64, _i64, _vp]),
     "nvfp4_last_error": (ctypes.c_char_p, []),

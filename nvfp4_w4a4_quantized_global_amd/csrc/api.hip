@@ -64,13 +64,15 @@ struct LinearWorkspace {
   size_t bytes;
 };
 
-LinearWorkspace carve(void* base, int64_t m, int64_t k, int64_t n) {
+// Layout of an nvfp4_linear workspace: codes, scales, amax partials, one global scale
+// per segment, then the GEMM's split-K partials; every piece 256-byte aligned.
+LinearWorkspace carve(void* base, int64_t m, int64_t k, int64_t n, int64_t segments = 1) {
   // offsets first, pointers only for a real base
   const size_t o_codes = 0;
   const size_t o_scales = align_up(o_codes + (size_t)m * (size_t)(k / 2));
   const size_t o_partials = align_up(o_scales + nvfp4_scale_bytes(m, k));
   const size_t o_gsf = align_up(o_partials + sizeof(float) * nvfp4::kMaxAmaxPartials);
-  const size_t o_gemm = align_up(o_gsf + sizeof(float));
+  const size_t o_gemm = align_up(o_gsf + sizeof(float) * (size_t)segments);
   const size_t gemm_bytes = nvfp4::gemm_workspace_bytes(m, k, n);
   LinearWorkspace w{nullptr, nullptr, nullptr, nullptr, nullptr, gemm_bytes, align_up(o_gemm + gemm_bytes)};
   if (base != nullptr) {
@@ -84,17 +86,59 @@ LinearWorkspace carve(void* base, int64_t m, int64_t k, int64_t n) {
   return w;
 }
 
+// Rows form `segments` consecutive blocks of m / segments rows; with a dynamic scale
+// each block gets its own global scale (gsf_out[segment]).
 int quantize_impl(const char* fn, const void* x, int64_t m, int64_t k, const float* gsf_static, int group,
-                  uint8_t* codes, uint8_t* scales, float* gsf_out, float* partials, hipStream_t s) {
+                  uint8_t* codes, uint8_t* scales, float* gsf_out, float* partials, hipStream_t s,
+                  int64_t segments = 1) {
   int n_partials = 0;
   const float c = inv_sqrt(group);
+  const int64_t seg_rows = m / segments;
   if (gsf_static == nullptr) {
-    int rc = hip_status(nvfp4::launch_amax_partials(static_cast<const uint16_t*>(x), m, k, group, c, partials,
-                                                    &n_partials, s), fn);
+    int rc = hip_status(nvfp4::launch_amax_partials(static_cast<const uint16_t*>(x), seg_rows, k, (int)segments,
+                                                    group, c, partials, &n_partials, s), fn);
     if (rc) return rc;
   }
   return hip_status(nvfp4::launch_quantize(static_cast<const uint16_t*>(x), m, k, group, c, gsf_static, partials,
-                                           n_partials, codes, scales, gsf_out, s), fn);
+                                           n_partials, seg_rows, (int)segments, codes, scales, gsf_out, s), fn);
+}
+
+int check_segments(const char* fn, int64_t segments, int64_t seg_rows) {
+  if (segments < 1 || segments > nvfp4::kMaxAmaxPartials)
+    return fail(NVFP4_ERR_ARG, "%s: segments must be in [1, %d], got %lld", fn, nvfp4::kMaxAmaxPartials,
+                (long long)segments);
+  if (seg_rows < 0 || (double)segments * (double)seg_rows >= (double)kMaxDim)
+    return fail(NVFP4_ERR_SHAPE, "%s: segments * seg_rows must be in [0, 2^31), got %lld * %lld", fn,
+                (long long)segments, (long long)seg_rows);
+  return NVFP4_OK;
+}
+
+// nvfp4_linear over `segments` row blocks of seg_rows rows (1 for a plain call).
+int linear_impl(const char* fn, const void* x, int64_t segments, int64_t seg_rows, int64_t k, const uint8_t* packed,
+                const uint8_t* inv_scale, const float* global_sf_w, const void* bias, int64_t out_features,
+                const float* global_sf_x, int rotation_group, void* out, float* gsf_out, void* workspace,
+                size_t workspace_bytes, hipStream_t s) {
+  const int64_t m = segments * seg_rows;
+  if (int rc = check_rows_k(fn, m, k, true)) return rc;
+  if (int rc = check_group(fn, rotation_group, k, true)) return rc;
+  if (out_features <= 0 || out_features >= kMaxDim)
+    return fail(NVFP4_ERR_SHAPE, "%s: out_features must be in [1, 2^31), got %lld", fn, (long long)out_features);
+  if (m == 0) return NVFP4_OK;
+  if (!x || !packed || !inv_scale || !global_sf_w || !out) return fail(NVFP4_ERR_ARG, "%s: NULL tensor argument", fn);
+  const size_t need = carve(nullptr, m, k, out_features, segments).bytes;
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % NVFP4_WORKSPACE_ALIGN))
+    return fail(NVFP4_ERR_WORKSPACE, "%s: need a %d-byte aligned workspace of %zu bytes, got %zu", fn,
+                NVFP4_WORKSPACE_ALIGN, need, workspace_bytes);
+  const LinearWorkspace ws = carve(workspace, m, k, out_features, segments);
+  float* gsf = gsf_out != nullptr ? gsf_out : ws.gsf;   // the GEMM reads the scales where they were written
+  const bool per_segment = global_sf_x == nullptr && segments > 1;
+  if (int rc = quantize_impl(fn, x, m, k, global_sf_x, rotation_group, ws.codes, ws.scales, gsf, ws.partials, s,
+                             per_segment ? segments : 1))
+    return rc;
+  return hip_status(nvfp4::launch_gemm(ws.codes, ws.scales, m, k, packed, inv_scale, out_features, gsf, global_sf_w,
+                                       per_segment ? seg_rows : 0, static_cast<const uint16_t*>(bias),
+                                       static_cast<uint16_t*>(out), ws.gemm, ws.gemm_bytes, s),
+                    fn);
 }
 
 }  // namespace
@@ -112,6 +156,11 @@ size_t nvfp4_quantize_workspace_bytes(void) { return align_up(sizeof(float) * nv
 size_t nvfp4_linear_workspace_bytes(int64_t m, int64_t k, int64_t n) {
   if (m < 0 || k <= 0 || n <= 0) return 0;
   return carve(nullptr, m, k, n).bytes;
+}
+
+size_t nvfp4_linear_segmented_workspace_bytes(int64_t segments, int64_t seg_rows, int64_t k, int64_t n) {
+  if (segments < 1 || segments > nvfp4::kMaxAmaxPartials || seg_rows < 0 || k <= 0 || n <= 0) return 0;
+  return carve(nullptr, segments * seg_rows, k, n, segments).bytes;
 }
 
 size_t nvfp4_gemm_workspace_bytes(int64_t m, int64_t k, int64_t n) {
@@ -170,6 +219,25 @@ int nvfp4_quantize_activation(const void* x, int64_t m, int64_t k, const float* 
                        static_cast<float*>(workspace), static_cast<hipStream_t>(stream));
 }
 
+int nvfp4_quantize_activation_segmented(const void* x, int64_t segments, int64_t seg_rows, int64_t k,
+                                        int rotation_group, uint8_t* codes, uint8_t* scales, float* gsf_out,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "nvfp4_quantize_activation_segmented";
+  g_err[0] = 0;
+  if (int rc = check_segments(fn, segments, seg_rows)) return rc;
+  const int64_t m = segments * seg_rows;
+  if (int rc = check_rows_k(fn, m, k, true)) return rc;
+  if (int rc = check_group(fn, rotation_group, k, true)) return rc;
+  if (m == 0) return NVFP4_OK;
+  if (!x || !codes || !scales || !gsf_out) return fail(NVFP4_ERR_ARG, "%s: NULL tensor argument", fn);
+  if (!workspace || workspace_bytes < nvfp4_quantize_workspace_bytes() ||
+      ((uintptr_t)workspace % NVFP4_WORKSPACE_ALIGN))
+    return fail(NVFP4_ERR_WORKSPACE, "%s: need a %d-byte aligned workspace of %zu bytes", fn, NVFP4_WORKSPACE_ALIGN,
+                nvfp4_quantize_workspace_bytes());
+  return quantize_impl(fn, x, m, k, nullptr, rotation_group, codes, scales, gsf_out, static_cast<float*>(workspace),
+                       static_cast<hipStream_t>(stream), segments);
+}
+
 int nvfp4_gemm(const uint8_t* x_codes, const uint8_t* x_scale, int64_t m, int64_t k, const uint8_t* packed,
                const uint8_t* inv_scale, int64_t n, const float* gsf_x, const float* gsf_w, const void* bias,
                void* out, void* workspace, size_t workspace_bytes, void* stream) {
@@ -182,7 +250,7 @@ int nvfp4_gemm(const uint8_t* x_codes, const uint8_t* x_scale, int64_t m, int64_
     return fail(NVFP4_ERR_ARG, "%s: NULL tensor argument", fn);
   if (workspace != nullptr && ((uintptr_t)workspace % NVFP4_WORKSPACE_ALIGN))
     return fail(NVFP4_ERR_WORKSPACE, "%s: workspace must be %d-byte aligned", fn, NVFP4_WORKSPACE_ALIGN);
-  return hip_status(nvfp4::launch_gemm(x_codes, x_scale, m, k, packed, inv_scale, n, gsf_x, gsf_w,
+  return hip_status(nvfp4::launch_gemm(x_codes, x_scale, m, k, packed, inv_scale, n, gsf_x, gsf_w, 0,
                                        static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(out), workspace,
                                        workspace != nullptr ? workspace_bytes : 0, static_cast<hipStream_t>(stream)),
                     fn);
@@ -191,26 +259,20 @@ int nvfp4_gemm(const uint8_t* x_codes, const uint8_t* x_scale, int64_t m, int64_
 int nvfp4_linear(const void* x, int64_t m, int64_t k, const uint8_t* packed, const uint8_t* inv_scale,
                  const float* global_sf_w, const void* bias, int64_t out_features, const float* global_sf_x,
                  int rotation_group, void* out, void* workspace, size_t workspace_bytes, void* stream) {
-  const char* fn = "nvfp4_linear";
   g_err[0] = 0;
-  if (int rc = check_rows_k(fn, m, k, true)) return rc;
-  if (int rc = check_group(fn, rotation_group, k, true)) return rc;
-  if (out_features <= 0 || out_features >= kMaxDim)
-    return fail(NVFP4_ERR_SHAPE, "%s: out_features must be in [1, 2^31), got %lld", fn, (long long)out_features);
-  if (m == 0) return NVFP4_OK;
-  if (!x || !packed || !inv_scale || !global_sf_w || !out) return fail(NVFP4_ERR_ARG, "%s: NULL tensor argument", fn);
-  const size_t need = nvfp4_linear_workspace_bytes(m, k, out_features);
-  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % NVFP4_WORKSPACE_ALIGN))
-    return fail(NVFP4_ERR_WORKSPACE, "%s: need a %d-byte aligned workspace of %zu bytes, got %zu", fn,
-                NVFP4_WORKSPACE_ALIGN, need, workspace_bytes);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const LinearWorkspace ws = carve(workspace, m, k, out_features);
-  if (int rc = quantize_impl(fn, x, m, k, global_sf_x, rotation_group, ws.codes, ws.scales, ws.gsf, ws.partials, s))
-    return rc;
-  return hip_status(nvfp4::launch_gemm(ws.codes, ws.scales, m, k, packed, inv_scale, out_features, ws.gsf,
-                                       global_sf_w, static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(out),
-                                       ws.gemm, ws.gemm_bytes, s),
-                    fn);
+  return linear_impl("nvfp4_linear", x, 1, m, k, packed, inv_scale, global_sf_w, bias, out_features, global_sf_x,
+                     rotation_group, out, nullptr, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+int nvfp4_linear_segmented(const void* x, int64_t segments, int64_t seg_rows, int64_t k, const uint8_t* packed,
+                           const uint8_t* inv_scale, const float* global_sf_w, const void* bias, int64_t out_features,
+                           int rotation_group, void* out, float* gsf_out, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  const char* fn = "nvfp4_linear_segmented";
+  g_err[0] = 0;
+  if (int rc = check_segments(fn, segments, seg_rows)) return rc;
+  return linear_impl(fn, x, segments, seg_rows, k, packed, inv_scale, global_sf_w, bias, out_features, nullptr,
+                     rotation_group, out, gsf_out, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 int nvfp4_scale_to_canonical(const uint8_t* layout, uint8_t* canonical, int64_t rows, int64_t k, void* stream) {

@@ -113,7 +113,8 @@ template <int WM, int WN, int TM, int TN>
 __global__ void __launch_bounds__(64 * WM * WN) gemm_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m, int64_t k,
     const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, int64_t n,
-    const float* __restrict__ gsf_a, const float* __restrict__ gsf_b, const uint16_t* __restrict__ bias,
+    const float* __restrict__ gsf_a, const float* __restrict__ gsf_b, int64_t a_seg_rows,
+    const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ out, int64_t b_srows, int64_t ldo, int tiles_m, int tiles_n, int aligned16) {
   using C = Cfg<WM, WN, TM, TN>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -228,19 +229,20 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_kernel(
 
   // Epilogue: y = bf16(alpha * acc) staged through LDS 32 rows at a time per wave,
   // then bf16(y + bias) written as 16-byte row segments.
-  const float alpha = __fdiv_rn(1.0f, __fmul_rn(*gsf_a, *gsf_b));
   uint8_t* epi = lds + wave * 32 * C::kEpiRowBytes;
   constexpr int kSegs = TN * 32 / 8;                 // 16-byte segments per staged row
   const int64_t wrow0 = row0 + wm * TM * 32;
   const int64_t wcol0 = col0 + wn * TN * 32;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
+    float al[16];
+    group_alphas(gsf_a, gsf_b, a_seg_rows, wrow0 + i * 32, kh, m, al);
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int r = 8 * (e >> 2) + 4 * kh + (e & 3);
-        const float y = __fmul_rn(alpha, __fmul_rn(acc[i][j][e], kAccUnscale));
+        const float y = __fmul_rn(al[e], __fmul_rn(acc[i][j][e], kAccUnscale));
         *reinterpret_cast<uint16_t*>(epi + r * C::kEpiRowBytes + (j * 32 + lr) * 2) = (uint16_t)f32_to_bf16(y);
       }
     }
@@ -278,7 +280,8 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_kernel(
 
 template <int WM, int WN, int TM, int TN>
 hipError_t launch_cfg(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, int64_t k, const uint8_t* b_codes,
-                      const uint8_t* b_scales, int64_t n, const float* gsf_a, const float* gsf_b, const uint16_t* bias,
+                      const uint8_t* b_scales, int64_t n, const float* gsf_a, const float* gsf_b, int64_t a_seg_rows,
+                      const uint16_t* bias,
                       uint16_t* out, int64_t b_srows, int64_t ldo, int aligned16, hipStream_t s) {
   using C = Cfg<WM, WN, TM, TN>;
   static bool attr_set = false;
@@ -291,7 +294,8 @@ hipError_t launch_cfg(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m
   const int tiles_m = (int)((m + C::BM - 1) / C::BM);
   const int tiles_n = (int)((n + C::BN - 1) / C::BN);
   hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN>), dim3(tiles_m * tiles_n), dim3(C::kThreads), C::kLds, s, a_codes,
-                     a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, out, b_srows, ldo, tiles_m, tiles_n, aligned16);
+                     a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, b_srows, ldo, tiles_m,
+                     tiles_n, aligned16);
   return hipGetLastError();
 }
 
@@ -299,15 +303,17 @@ hipError_t launch_cfg(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m
 // b_srows rows per K tile and whose output rows are ldo elements apart.
 hipError_t launch_generic(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, int64_t k,
                           const uint8_t* b_codes, const uint8_t* b_scales, int64_t n, const float* gsf_a,
-                          const float* gsf_b, const uint16_t* bias, uint16_t* out, int64_t b_srows, int64_t ldo,
-                          int cus, hipStream_t s) {
+                          const float* gsf_b, int64_t a_seg_rows, const uint16_t* bias, uint16_t* out,
+                          int64_t b_srows, int64_t ldo, int cus, hipStream_t s) {
   const int aligned16 = ((k / 2) % 16 == 0) && (((uintptr_t)a_codes | (uintptr_t)b_codes) % 16 == 0);
   // Largest tile that still gives every compute unit a tile.
   const int64_t mid = ((m + 255) / 256) * ((n + 127) / 128);
   if (mid >= cus)
-    return launch_cfg<2, 2, 4, 2>(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, out, b_srows, ldo,
+    return launch_cfg<2, 2, 4, 2>(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out,
+                                  b_srows, ldo,
                                   aligned16, s);
-  return launch_cfg<2, 2, 2, 2>(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, out, b_srows, ldo,
+  return launch_cfg<2, 2, 2, 2>(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out,
+                                b_srows, ldo,
                                 aligned16, s);
 }
 
@@ -342,16 +348,17 @@ size_t gemm_workspace_bytes(int64_t m, int64_t k, int64_t n) {
 
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, int64_t k,
                        const uint8_t* b_codes, const uint8_t* b_scales, int64_t n,
-                       const float* gsf_a, const float* gsf_b, const uint16_t* bias, uint16_t* out,
-                       void* workspace, size_t workspace_bytes, hipStream_t s) {
+                       const float* gsf_a, const float* gsf_b, int64_t a_seg_rows, const uint16_t* bias,
+                       uint16_t* out, void* workspace, size_t workspace_bytes, hipStream_t s) {
   const int cus = compute_units();
   if (prefer_skinny(m, n) && gemm_skinny_supported(m, k, a_codes, a_scales, b_codes, b_scales))
-    return launch_gemm_skinny(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, out, workspace,
-                              workspace_bytes, cus, s);
+    return launch_gemm_skinny(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out,
+                              workspace, workspace_bytes, cus, s);
   if (gemm_pipe_supported(m, k, n, a_codes, a_scales, b_codes, b_scales, cus))
-    return launch_gemm_pipe(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, out, workspace,
-                            workspace_bytes, cus, s);
-  return launch_generic(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, out, n, n, cus, s);
+    return launch_gemm_pipe(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out,
+                            workspace, workspace_bytes, cus, s);
+  return launch_generic(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, n, n, cus,
+                        s);
 }
 
 }  // namespace nvfp4

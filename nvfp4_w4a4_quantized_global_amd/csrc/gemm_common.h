@@ -46,6 +46,33 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int s) {
   return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w;
 }
 
+// alpha = fp32(1 / fp32(gsf_a * gsf_b)).  With seg_rows > 0 the activation rows come in
+// blocks of seg_rows rows with one global scale each, gsf_a[row / seg_rows].
+__device__ __forceinline__ float alpha_for(const float* gsf_a, const float* gsf_b, int64_t seg_rows, int64_t row) {
+  const float ga = seg_rows > 0 ? gsf_a[row / seg_rows] : *gsf_a;
+  return __fdiv_rn(1.0f, __fmul_rn(ga, *gsf_b));
+}
+
+// The 16 alphas of the rows 8*(e/4) + 4*kh + e%4 (e = 0..15) of a 32-row MFMA output
+// group starting at row g0 (rows clamped to m - 1): one value when the group lies in
+// one segment, the common case.
+__device__ __forceinline__ void group_alphas(const float* gsf_a, const float* gsf_b, int64_t seg_rows, int64_t g0,
+                                             int kh, int64_t m, float (&al)[16]) {
+  const int64_t first = g0 < m - 1 ? g0 : m - 1;
+  const int64_t last = g0 + 31 < m - 1 ? g0 + 31 : m - 1;
+  if (seg_rows <= 0 || first / seg_rows == last / seg_rows) {
+    const float a = alpha_for(gsf_a, gsf_b, seg_rows, first);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) al[e] = a;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t r = g0 + 8 * (e >> 2) + 4 * kh + (e & 3);
+      al[e] = alpha_for(gsf_a, gsf_b, seg_rows, r < m - 1 ? r : m - 1);
+    }
+  }
+}
+
 // bf16(y) + bias in fp32, rounded to bf16: the bias add after the GEMM output is rounded.
 __device__ __forceinline__ uint32_t add_bias_bf16(uint32_t y_bf16, uint16_t bias_bf16) {
   return f32_to_bf16(__fadd_rn(bf16_to_f32(y_bf16), bf16_to_f32(bias_bf16)));

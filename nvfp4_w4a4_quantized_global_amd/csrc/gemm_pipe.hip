@@ -90,8 +90,9 @@ template <bool kSplit>
 __global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m, int64_t k,
     const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, int64_t n,
-    const float* __restrict__ gsf_a, const float* __restrict__ gsf_b, const uint16_t* __restrict__ bias,
-    uint16_t* __restrict__ out, int64_t b_srows, int64_t ldo, int tiles_m, int tiles_n, int tile0, int splits,
+    const float* __restrict__ gsf_a, const float* __restrict__ gsf_b, int64_t a_seg_rows,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int64_t b_srows, int64_t ldo, int tiles_m,
+    int tiles_n, int tile0, int splits,
     float* __restrict__ partial) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   // Tile indices follow tile_coords.  Without split-K, workgroups (dealt round-robin to
@@ -297,18 +298,19 @@ __global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
 
   // Epilogue: bf16(alpha * acc) staged through LDS 32 rows per wave at a time, then
   // bf16(y + bias), written as 16-byte row segments.
-  const float alpha = __fdiv_rn(1.0f, __fmul_rn(*gsf_a, *gsf_b));
   uint8_t* epi = lds + wave * 32 * kEpiRowBytes;
   const int64_t wrow0 = row0 + wm * 128;
   const int64_t wcol0 = col0 + wn * 128;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    float al[16];
+    group_alphas(gsf_a, gsf_b, a_seg_rows, wrow0 + i * 32, kh, m, al);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int r = 8 * (e >> 2) + 4 * kh + (e & 3);
-        const float y = __fmul_rn(alpha, __fmul_rn(acc[i][j][e], kAccUnscale));
+        const float y = __fmul_rn(al[e], __fmul_rn(acc[i][j][e], kAccUnscale));
         *reinterpret_cast<uint16_t*>(epi + r * kEpiRowBytes + (j * 32 + lr) * 2) = (uint16_t)f32_to_bf16(y);
       }
     }
@@ -349,8 +351,8 @@ __global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
 __global__ void __launch_bounds__(256) split_k_reduce(const float* __restrict__ partial, int splits, int tiles,
                                                       int tile0, int tiles_m, int64_t m, int64_t n,
                                                       const float* __restrict__ gsf_a, const float* __restrict__ gsf_b,
-                                                      const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
-                                                      int64_t ldo) {
+                                                      int64_t a_seg_rows, const uint16_t* __restrict__ bias,
+                                                      uint16_t* __restrict__ out, int64_t ldo) {
   const int tl = blockIdx.x >> 8;         // tile within the split launch
   const int q = blockIdx.x & 255;         // accumulator entry (i, j, e) of the owning thread
   const int t = threadIdx.x;              // owning thread of the main kernel
@@ -366,7 +368,7 @@ __global__ void __launch_bounds__(256) split_k_reduce(const float* __restrict__ 
   const int64_t row = row0 + (wave >> 1) * 128 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
   const int64_t col = col0 + (wave & 1) * 128 + j * 32 + (lane & 31);
   if (row >= m || col >= n) return;
-  const float alpha = __fdiv_rn(1.0f, __fmul_rn(*gsf_a, *gsf_b));
+  const float alpha = alpha_for(gsf_a, gsf_b, a_seg_rows, row);
   uint32_t y = f32_to_bf16(__fmul_rn(alpha, __fmul_rn(acc, kAccUnscale)));
   if (bias != nullptr) y = add_bias_bf16(y, bias[col]);
   out[row * ldo + col] = (uint16_t)y;
@@ -415,8 +417,8 @@ size_t gemm_pipe_workspace_bytes(int64_t m, int64_t k, int64_t n, int cus) {
 
 hipError_t launch_gemm_pipe(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, int64_t k,
                             const uint8_t* b_codes, const uint8_t* b_scales, int64_t n, const float* gsf_a,
-                            const float* gsf_b, const uint16_t* bias, uint16_t* out, void* workspace,
-                            size_t workspace_bytes, int cus, hipStream_t s) {
+                            const float* gsf_b, int64_t a_seg_rows, const uint16_t* bias, uint16_t* out,
+                            void* workspace, size_t workspace_bytes, int cus, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_pipe_kernel<false>),
@@ -433,7 +435,7 @@ hipError_t launch_gemm_pipe(const uint8_t* a_codes, const uint8_t* a_scales, int
   const int tm = (int)p.tiles_m, tn = (int)p.tiles_n;
   if (p.full > 0) {
     hipLaunchKernelGGL(gemm_pipe_kernel<false>, dim3((uint32_t)p.full), dim3(256), kLds, s, a_codes, a_scales, m, k, b_codes,
-                       b_scales, n, gsf_a, gsf_b, bias, out, n, n, tm, tn, 0, 1, (float*)nullptr);
+                       b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, n, n, tm, tn, 0, 1, (float*)nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -441,16 +443,16 @@ hipError_t launch_gemm_pipe(const uint8_t* a_codes, const uint8_t* a_scales, int
   float* partial = static_cast<float*>(workspace);
   if (p.splits == 1) {
     hipLaunchKernelGGL(gemm_pipe_kernel<false>, dim3((uint32_t)p.rest), dim3(256), kLds, s, a_codes, a_scales, m, k,
-                       b_codes, b_scales, n, gsf_a, gsf_b, bias, out, n, n, tm, tn, (int)p.full, 1, (float*)nullptr);
+                       b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, n, n, tm, tn, (int)p.full, 1, (float*)nullptr);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(gemm_pipe_kernel<true>, dim3((uint32_t)(p.rest * p.splits)), dim3(256), kLds, s, a_codes,
-                     a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, out, n, n, tm, tn, (int)p.full,
+                     a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, n, n, tm, tn, (int)p.full,
                      p.splits, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(split_k_reduce, dim3((uint32_t)(p.rest * 256)), dim3(256), 0, s, partial, p.splits, (int)p.rest,
-                     (int)p.full, tm, m, n, gsf_a, gsf_b, bias, out, n);
+                     (int)p.full, tm, m, n, gsf_a, gsf_b, a_seg_rows, bias, out, n);
   return hipGetLastError();
 }
 

@@ -39,8 +39,8 @@ template <int MT>   // M tiles of 16 rows
 __global__ void __launch_bounds__(256) gemm_skinny_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m, int64_t k,
     const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, int64_t n,
-    const float* __restrict__ gsf_a, const float* __restrict__ gsf_b, const uint16_t* __restrict__ bias,
-    uint16_t* __restrict__ out, int splits, float* __restrict__ partial) {
+    const float* __restrict__ gsf_a, const float* __restrict__ gsf_b, int64_t a_seg_rows,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int splits, float* __restrict__ partial) {
   __shared__ float red[MT * 4][4][64];     // waves 1..3 hand their sums to wave 0, one at a time
 
   const int col_group = blockIdx.x / splits;
@@ -158,7 +158,7 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(
   if (wave != 0) return;
 
   // 16x16 MFMA output: lane holds column l16 of each tile, rows 4g .. 4g+3.
-  const float alpha = __fdiv_rn(1.0f, __fmul_rn(*gsf_a, *gsf_b));
+  const float alpha = __fdiv_rn(1.0f, __fmul_rn(*gsf_a, *gsf_b));   // one activation scale
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int64_t col = n0 + 16 * j + l16;
@@ -172,7 +172,8 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(
         if (splits > 1) {
           partial[((int64_t)split * m + row) * n + col] = acc[i][j][e];
         } else {
-          uint32_t y = f32_to_bf16(__fmul_rn(alpha, __fmul_rn(acc[i][j][e], kAccUnscale)));
+          const float al = a_seg_rows > 0 ? alpha_for(gsf_a, gsf_b, a_seg_rows, row) : alpha;
+          uint32_t y = f32_to_bf16(__fmul_rn(al, __fmul_rn(acc[i][j][e], kAccUnscale)));
           if (bias != nullptr) y = add_bias_bf16(y, bias[col]);
           out[row * n + col] = (uint16_t)y;
         }
@@ -184,13 +185,13 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(
 // Sums the per-split partials [splits][m][n] in split order, then the epilogue.
 __global__ void __launch_bounds__(256) gemm_skinny_reduce(const float* __restrict__ partial, int splits, int64_t m,
                                                           int64_t n, const float* __restrict__ gsf_a,
-                                                          const float* __restrict__ gsf_b,
+                                                          const float* __restrict__ gsf_b, int64_t a_seg_rows,
                                                           const uint16_t* __restrict__ bias, uint16_t* __restrict__ out) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= m * n) return;
   float acc = 0.0f;
   for (int sp = 0; sp < splits; ++sp) acc += partial[sp * m * n + idx];
-  const float alpha = __fdiv_rn(1.0f, __fmul_rn(*gsf_a, *gsf_b));
+  const float alpha = alpha_for(gsf_a, gsf_b, a_seg_rows, idx / n);
   uint32_t y = f32_to_bf16(__fmul_rn(alpha, __fmul_rn(acc, kAccUnscale)));
   if (bias != nullptr) y = add_bias_bf16(y, bias[idx % n]);
   out[idx] = (uint16_t)y;
@@ -210,10 +211,10 @@ int skinny_splits(int64_t k, int64_t n, int cus) {
 template <int MT>
 hipError_t launch_mt(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, int64_t k, const uint8_t* b_codes,
                      const uint8_t* b_scales, int64_t n, const float* gsf_a, const float* gsf_b, const uint16_t* bias,
-                     uint16_t* out, int splits, float* partial, hipStream_t s) {
+                     int64_t a_seg_rows, uint16_t* out, int splits, float* partial, hipStream_t s) {
   const int64_t groups = (n + kCols - 1) / kCols;
   hipLaunchKernelGGL(gemm_skinny_kernel<MT>, dim3((uint32_t)(groups * splits)), dim3(256), 0, s, a_codes, a_scales,
-                     m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, out, splits, partial);
+                     m, k, b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, splits, partial);
   return hipGetLastError();
 }
 
@@ -232,21 +233,21 @@ size_t gemm_skinny_workspace_bytes(int64_t m, int64_t k, int64_t n, int cus) {
 
 hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, int64_t k,
                               const uint8_t* b_codes, const uint8_t* b_scales, int64_t n, const float* gsf_a,
-                              const float* gsf_b, const uint16_t* bias, uint16_t* out, void* workspace,
-                              size_t workspace_bytes, int cus, hipStream_t s) {
+                              const float* gsf_b, int64_t a_seg_rows, const uint16_t* bias, uint16_t* out,
+                              void* workspace, size_t workspace_bytes, int cus, hipStream_t s) {
   int splits = skinny_splits(k, n, cus);
   const size_t need = splits > 1 ? (size_t)splits * (size_t)m * (size_t)n * sizeof(float) : 0;
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) splits = 1;
   float* partial = splits > 1 ? static_cast<float*>(workspace) : nullptr;
   hipError_t e;
-  if (m <= 16) e = launch_mt<1>(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, out, splits, partial, s);
-  else if (m <= 32) e = launch_mt<2>(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, out, splits, partial, s);
-  else if (m <= 64) e = launch_mt<4>(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, out, splits, partial, s);
-  else e = launch_mt<8>(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, out, splits, partial, s);
+  if (m <= 16) e = launch_mt<1>(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, a_seg_rows, out, splits, partial, s);
+  else if (m <= 32) e = launch_mt<2>(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, a_seg_rows, out, splits, partial, s);
+  else if (m <= 64) e = launch_mt<4>(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, a_seg_rows, out, splits, partial, s);
+  else e = launch_mt<8>(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, a_seg_rows, out, splits, partial, s);
   if (e != hipSuccess || splits == 1) return e;
   const int64_t total = m * n;
   hipLaunchKernelGGL(gemm_skinny_reduce, dim3((uint32_t)((total + 255) / 256)), dim3(256), 0, s, partial, splits, m,
-                     n, gsf_a, gsf_b, bias, out);
+                     n, gsf_a, gsf_b, a_seg_rows, bias, out);
   return hipGetLastError();
 }
 

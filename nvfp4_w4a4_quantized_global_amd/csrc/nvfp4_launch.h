@@ -11,12 +11,17 @@ namespace nvfp4 {
 // Upper bound on the number of per-block partial maxima of the amax pass.
 constexpr int kMaxAmaxPartials = 1024;
 
-hipError_t launch_amax_partials(const uint16_t* x, int64_t rows, int64_t k, int group, float inv_sqrt_g,
-                                float* partials, int* n_partials, hipStream_t s);
+// Partial maxima of `segments` consecutive row blocks of seg_rows rows each (one
+// segment for a plain call): partials[seg * (*n_partials) + i].
+hipError_t launch_amax_partials(const uint16_t* x, int64_t seg_rows, int64_t k, int segments, int group,
+                                float inv_sqrt_g, float* partials, int* n_partials, hipStream_t s);
 
+// Quantizes rows x [rows][k]; with static_gsf NULL, segment s (rows [s*seg_rows,
+// (s+1)*seg_rows)) takes its global scale from its n_partials partial maxima and
+// gsf_out[s] receives it.
 hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t k, int group, float inv_sqrt_g,
-                           const float* static_gsf, const float* partials, int n_partials,
-                           uint8_t* codes, uint8_t* scales, float* gsf_out, hipStream_t s);
+                           const float* static_gsf, const float* partials, int n_partials, int64_t seg_rows,
+                           int segments, uint8_t* codes, uint8_t* scales, float* gsf_out, hipStream_t s);
 
 hipError_t launch_rotate(const void* x, bool x_bf16, void* y, bool y_bf16, int64_t rows, int64_t k, int group,
                          float inv_sqrt_g, hipStream_t s);
@@ -24,10 +29,12 @@ hipError_t launch_rotate(const void* x, bool x_bf16, void* y, bool y_bf16, int64
 hipError_t launch_scale_layout(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t k, bool to_canonical,
                                hipStream_t s);
 
+// alpha = 1 / (gsf_a * gsf_b); with a_seg_rows > 0, row r of A takes gsf_a[r / a_seg_rows]
+// (one global scale per block of a_seg_rows rows), otherwise gsf_a[0] for every row.
 hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, int64_t k,
                        const uint8_t* b_codes, const uint8_t* b_scales, int64_t n,
-                       const float* gsf_a, const float* gsf_b, const uint16_t* bias, uint16_t* out,
-                       void* workspace, size_t workspace_bytes, hipStream_t s);
+                       const float* gsf_a, const float* gsf_b, int64_t a_seg_rows, const uint16_t* bias,
+                       uint16_t* out, void* workspace, size_t workspace_bytes, hipStream_t s);
 
 // Compute units of the current device (cached per device).
 int compute_units();
@@ -41,8 +48,8 @@ bool gemm_pipe_supported(int64_t m, int64_t k, int64_t n, const void* a_codes, c
 size_t gemm_pipe_workspace_bytes(int64_t m, int64_t k, int64_t n, int cus);
 hipError_t launch_gemm_pipe(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, int64_t k,
                             const uint8_t* b_codes, const uint8_t* b_scales, int64_t n, const float* gsf_a,
-                            const float* gsf_b, const uint16_t* bias, uint16_t* out, void* workspace,
-                            size_t workspace_bytes, int cus, hipStream_t s);
+                            const float* gsf_b, int64_t a_seg_rows, const uint16_t* bias, uint16_t* out,
+                            void* workspace, size_t workspace_bytes, int cus, hipStream_t s);
 
 // The weight-streaming GEMM for m <= 128 (gemm_skinny.hip): K a multiple of 32, code
 // pointers 16-byte and scale pointers 4-byte aligned.  Splits K across blocks when the
@@ -52,8 +59,8 @@ bool gemm_skinny_supported(int64_t m, int64_t k, const void* a_codes, const void
 size_t gemm_skinny_workspace_bytes(int64_t m, int64_t k, int64_t n, int cus);
 hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, int64_t k,
                               const uint8_t* b_codes, const uint8_t* b_scales, int64_t n, const float* gsf_a,
-                              const float* gsf_b, const uint16_t* bias, uint16_t* out, void* workspace,
-                              size_t workspace_bytes, int cus, hipStream_t s);
+                              const float* gsf_b, int64_t a_seg_rows, const uint16_t* bias, uint16_t* out,
+                              void* workspace, size_t workspace_bytes, int cus, hipStream_t s);
 
 // Workspace the GEMM dispatcher can use for an [m, k] x [n, k] product (0 if none).
 size_t gemm_workspace_bytes(int64_t m, int64_t k, int64_t n);

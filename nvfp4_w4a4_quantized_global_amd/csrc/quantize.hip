@@ -65,11 +65,14 @@ __device__ __forceinline__ float block_max(float x, float* lds) {
 // kAmaxUnroll chunks in flight.
 constexpr int kAmaxUnroll = 4;
 
+// Segments (blockIdx.y) are consecutive row blocks of n_chunks chunks each, reduced
+// separately into partials[blockIdx.y * gridDim.x + blockIdx.x].
 template <bool kRotate>
 __global__ void __launch_bounds__(kThreads) amax_partial_kernel(const uint16_t* __restrict__ x, int64_t n_chunks,
                                                                  int group, float inv_sqrt_g,
                                                                  float* __restrict__ partials) {
   __shared__ float lds[kThreads / 64];
+  x += (int64_t)blockIdx.y * n_chunks * 16;
   float m = 0.0f;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   for (int64_t c0 = (int64_t)blockIdx.x * kThreads; c0 < n_chunks; c0 += stride * kAmaxUnroll) {
@@ -92,7 +95,7 @@ __global__ void __launch_bounds__(kThreads) amax_partial_kernel(const uint16_t* 
     }
   }
   m = block_max(m, lds);
-  if (threadIdx.x == 0) partials[blockIdx.x] = m;
+  if (threadIdx.x == 0) partials[blockIdx.y * gridDim.x + blockIdx.x] = m;
 }
 
 // Pass 2: quantize.  Eight consecutive lanes own one 128-wide K tile of one row
@@ -104,26 +107,39 @@ __global__ void __launch_bounds__(kThreads) amax_partial_kernel(const uint16_t* 
 constexpr int kQuantUnits = 2;
 constexpr int kQuantBlocks = 2048;   // grid cap: blocks loop over the units
 
+// With a dynamic scale the rows form `segments` consecutive blocks of seg_rows rows,
+// each with its own global scale from its own n_partials partial maxima (one segment
+// for a plain call); gsf_out receives one scale per segment.
 template <bool kRotate>
 __global__ void __launch_bounds__(kThreads) quantize_kernel(
     const uint16_t* __restrict__ x, int64_t m_rows, int64_t k, int group, float inv_sqrt_g,
-    const float* __restrict__ static_gsf, const float* __restrict__ partials, int n_partials,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gsf_out) {
-  __shared__ float lds[kThreads / 64];
+    const float* __restrict__ static_gsf, const float* __restrict__ partials, int n_partials, int64_t seg_rows,
+    int segments, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gsf_out) {
+  __shared__ uint32_t seg_amax[kMaxAmaxPartials];   // segment maxima, then global scales (bits)
   const int64_t kt_count = (k + kScaleTileK - 1) / kScaleTileK;
   const int64_t nb = k / kBlock;
   const int j = threadIdx.x & 7;
 
-  float gsf;
-  if (static_gsf != nullptr) {
-    gsf = *static_gsf;
-  } else {
-    float a = 0.0f;
-    for (int i = threadIdx.x; i < n_partials; i += kThreads) a = fmaxf(a, partials[i]);
-    a = block_max(a, lds);
-    gsf = global_scale_from_amax(a);
+  const bool dynamic = static_gsf == nullptr;
+  const float gsf_static = dynamic ? 0.0f : *static_gsf;
+  if (dynamic) {
+    // max of non-negative floats = max of their bit patterns
+    for (int i = threadIdx.x; i < segments; i += kThreads) seg_amax[i] = 0u;
+    __syncthreads();
+    for (int i = threadIdx.x; i < segments * n_partials; i += kThreads)
+      atomicMax(&seg_amax[i / n_partials], __float_as_uint(partials[i]));
+    __syncthreads();
+    for (int i = threadIdx.x; i < segments; i += kThreads)
+      seg_amax[i] = __float_as_uint(global_scale_from_amax(__uint_as_float(seg_amax[i])));
+    __syncthreads();
   }
-  if (gsf_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *gsf_out = gsf;
+  if (gsf_out != nullptr && blockIdx.x == 0) {
+    if (dynamic) {
+      for (int i = threadIdx.x; i < segments; i += kThreads) gsf_out[i] = __uint_as_float(seg_amax[i]);
+    } else if (threadIdx.x == 0) {
+      *gsf_out = gsf_static;
+    }
+  }
 
   const int64_t units_total = m_rows * kt_count;
   const int64_t per_block = (int64_t)kQuantUnits * (kThreads / 8);
@@ -150,6 +166,7 @@ __global__ void __launch_bounds__(kThreads) quantize_kernel(
       const int64_t blk = kt[u] * 8 + j;
       const bool in_row = row[u] < m_rows;
       const bool valid = in_row && blk < nb;
+      const float gsf = dynamic ? __uint_as_float(seg_amax[in_row ? row[u] / seg_rows : 0]) : gsf_static;
       float bmax = 0.0f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) bmax = fmaxf(bmax, fabsf(v[u][i]));
@@ -243,21 +260,24 @@ int64_t grid_for(int64_t n_chunks, int64_t cap) {
 
 }  // namespace
 
-hipError_t launch_amax_partials(const uint16_t* x, int64_t rows, int64_t k, int group, float inv_sqrt_g,
-                                float* partials, int* n_partials, hipStream_t s) {
-  const int64_t n_chunks = rows * k / kBlock;
-  const int grid = (int)grid_for((n_chunks + kAmaxUnroll - 1) / kAmaxUnroll, kAmaxBlocks);
+hipError_t launch_amax_partials(const uint16_t* x, int64_t seg_rows, int64_t k, int segments, int group,
+                                float inv_sqrt_g, float* partials, int* n_partials, hipStream_t s) {
+  const int64_t n_chunks = seg_rows * k / kBlock;
+  int64_t cap = kAmaxBlocks / segments;
+  if (cap < 1) cap = 1;
+  const int grid = (int)grid_for((n_chunks + kAmaxUnroll - 1) / kAmaxUnroll, cap);
   *n_partials = grid;
+  const dim3 g3((uint32_t)grid, (uint32_t)segments);
   if (group > 1)
-    hipLaunchKernelGGL(amax_partial_kernel<true>, dim3(grid), dim3(kThreads), 0, s, x, n_chunks, group, inv_sqrt_g, partials);
+    hipLaunchKernelGGL(amax_partial_kernel<true>, g3, dim3(kThreads), 0, s, x, n_chunks, group, inv_sqrt_g, partials);
   else
-    hipLaunchKernelGGL(amax_partial_kernel<false>, dim3(grid), dim3(kThreads), 0, s, x, n_chunks, group, inv_sqrt_g, partials);
+    hipLaunchKernelGGL(amax_partial_kernel<false>, g3, dim3(kThreads), 0, s, x, n_chunks, group, inv_sqrt_g, partials);
   return hipGetLastError();
 }
 
 hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t k, int group, float inv_sqrt_g,
-                           const float* static_gsf, const float* partials, int n_partials,
-                           uint8_t* codes, uint8_t* scales, float* gsf_out, hipStream_t s) {
+                           const float* static_gsf, const float* partials, int n_partials, int64_t seg_rows,
+                           int segments, uint8_t* codes, uint8_t* scales, float* gsf_out, hipStream_t s) {
   const int64_t kt_count = (k + kScaleTileK - 1) / kScaleTileK;
   const int64_t units = rows * kt_count;
   const int64_t per_block = (int64_t)kQuantUnits * (kThreads / 8);
@@ -265,10 +285,10 @@ hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t k, int group
   if (grid > kQuantBlocks) grid = kQuantBlocks;
   if (group > 1)
     hipLaunchKernelGGL(quantize_kernel<true>, dim3((uint32_t)grid), dim3(kThreads), 0, s, x, rows, k, group, inv_sqrt_g,
-                       static_gsf, partials, n_partials, codes, scales, gsf_out);
+                       static_gsf, partials, n_partials, seg_rows, segments, codes, scales, gsf_out);
   else
     hipLaunchKernelGGL(quantize_kernel<false>, dim3((uint32_t)grid), dim3(kThreads), 0, s, x, rows, k, group, inv_sqrt_g,
-                       static_gsf, partials, n_partials, codes, scales, gsf_out);
+                       static_gsf, partials, n_partials, seg_rows, segments, codes, scales, gsf_out);
   return hipGetLastError();
 }
 

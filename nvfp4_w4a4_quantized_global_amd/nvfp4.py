@@ -54,6 +54,11 @@ def linear_workspace_bytes(m: int, k: int, n: int) -> int:
     return int(lib().nvfp4_linear_workspace_bytes(m, k, n))
 
 
+def linear_segmented_workspace_bytes(segments: int, seg_rows: int, k: int, n: int) -> int:
+    """Workspace of nvfp4_linear_segmented (current device)."""
+    return int(lib().nvfp4_linear_segmented_workspace_bytes(segments, seg_rows, k, n))
+
+
 def gemm_workspace_bytes(m: int, k: int, n: int) -> int:
     """Workspace nvfp4_gemm can use to split the last round of tiles along K (current device)."""
     return int(lib().nvfp4_gemm_workspace_bytes(m, k, n))
@@ -199,6 +204,74 @@ def nvfp4_linear(x: torch.Tensor, packed: torch.Tensor, inv_scale: torch.Tensor,
     return out.reshape(*orig[:-1], out_features)
 
 
+def _segment_rows(x2d: torch.Tensor, segments: int) -> int:
+    if not 1 <= int(segments) <= 1024:
+        raise ValueError(f"segments must be in [1, 1024], got {segments}")
+    if x2d.shape[0] % segments:
+        raise ValueError(f"{x2d.shape[0]} rows do not split into {segments} equal segments")
+    return x2d.shape[0] // segments
+
+
+def quantize_activation_segmented(x: torch.Tensor, segments: int, rotation_group: int = 0
+                                  ) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Dynamic-scale quantization of ``segments`` equal row blocks, one global scale each.
+
+    Returns codes uint8 [M, K/2], scales (layout of the whole [M, K] input) and the
+    per-segment global scales, fp32 [segments]."""
+    _require_cuda("x", x, torch.bfloat16, 2)
+    m, k = x.shape
+    seg_rows = _segment_rows(x, segments)
+    codes = torch.empty((m, k // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((max(scale_bytes(m, k), 1),), dtype=torch.uint8, device=x.device)
+    gsf = torch.empty((segments,), dtype=torch.float32, device=x.device)
+    ws = torch.empty((quantize_workspace_bytes(),), dtype=torch.uint8, device=x.device)
+    check(lib().nvfp4_quantize_activation_segmented(_ptr(x), segments, seg_rows, k, int(rotation_group), _ptr(codes),
+                                                    _ptr(scales), _ptr(gsf), _ptr(ws), ws.numel(), _stream(x.device)))
+    return codes, scales[: scale_bytes(m, k)], gsf
+
+
+def nvfp4_linear_segmented(x: torch.Tensor, segments: int, packed: torch.Tensor, inv_scale: torch.Tensor,
+                           global_sf_w: torch.Tensor, bias: torch.Tensor | None, out_features: int,
+                           rotation_group: int = 0, workspace: torch.Tensor | None = None,
+                           out: torch.Tensor | None = None, gsf_out: torch.Tensor | None = None) -> torch.Tensor:
+    """nvfp4_linear over ``segments`` equal row blocks (tiles) of x in one pass, each tile
+    with its own dynamic activation scale, as separate per-tile calls would give."""
+    if x.dtype != torch.bfloat16:
+        raise ValueError(f"x must be bf16, got {x.dtype}")
+    k = x.shape[-1]
+    x2d = x.reshape(-1, k)
+    if not x2d.is_contiguous():
+        x2d = x2d.contiguous()
+    _require_cuda("x", x2d, torch.bfloat16, 2)
+    seg_rows = _segment_rows(x2d, segments)
+    _require_cuda("packed", packed, torch.uint8, 2)
+    if packed.shape[0] != out_features or packed.shape[1] * 2 != k:
+        raise ValueError(f"packed NVFP4 weight must be uint8 [{out_features}, {k // 2}], got "
+                         f"{packed.dtype} {list(packed.shape)}")
+    _require_cuda("inv_scale", inv_scale, torch.uint8)
+    if inv_scale.numel() < scale_bytes(out_features, k):
+        raise ValueError("inv_scale is smaller than nvfp4_scale_bytes(out_features, K)")
+    gw = _scalar_f32(global_sf_w, x.device)
+    if bias is not None:
+        _require_cuda("bias", bias, torch.bfloat16)
+        if bias.numel() != out_features:
+            raise ValueError(f"bias must have {out_features} elements, got {bias.numel()}")
+    if gsf_out is not None:
+        _require_cuda("gsf_out", gsf_out, torch.float32)
+        if gsf_out.numel() < segments:
+            raise ValueError(f"gsf_out must hold {segments} values")
+    m = x2d.shape[0]
+    need = linear_segmented_workspace_bytes(segments, seg_rows, k, out_features)
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((m, out_features), dtype=torch.bfloat16, device=x.device)
+    check(lib().nvfp4_linear_segmented(_ptr(x2d), segments, seg_rows, k, _ptr(packed), _ptr(inv_scale), _ptr(gw),
+                                       _ptr(bias), out_features, int(rotation_group), _ptr(out), _ptr(gsf_out),
+                                       _ptr(workspace), workspace.numel(), _stream(x.device)))
+    return out.reshape(*x.shape[:-1], out_features)
+
+
 def scale_to_canonical(layout: torch.Tensor, rows: int, k: int) -> torch.Tensor:
     """Block scales from the library layout to row-major uint8 [rows, K/16]."""
     _require_cuda("layout", layout, torch.uint8)
@@ -283,3 +356,12 @@ class NVFP4Linear:
     def __call__(self, x: torch.Tensor) -> torch.Tensor:
         return nvfp4_linear(x.to(torch.bfloat16), self.packed, self.inv_scale, self.global_sf_w, self.bias,
                             self.out_features, self.activation_global_sf(), self.rotation_group or 0)
+
+    def forward_tiles(self, x: torch.Tensor, tiles: int) -> torch.Tensor:
+        """x holds ``tiles`` equal row blocks (decoder tiles); one pass over all of them
+        with the result of calling the layer on each tile alone.  With a dynamic scale
+        every tile keeps its own global scale; static and unit scales are shared anyway."""
+        if self.act_scale != "dynamic":
+            return self(x)
+        return nvfp4_linear_segmented(x.to(torch.bfloat16), tiles, self.packed, self.inv_scale, self.global_sf_w,
+                                      self.bias, self.out_features, self.rotation_group or 0)

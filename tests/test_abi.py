@@ -92,6 +92,21 @@ def test_null_arguments():
     assert lib().rotate_activation(FAKE, 5, FAKE, 0, 2, 64, 16, None) == NVFP4_ERR_ARG
 
 
+def test_segmented_arguments():
+    L = lib()
+    assert L.nvfp4_linear_segmented_workspace_bytes(8, 4096, 1024, 4096) >= L.nvfp4_linear_workspace_bytes(32768, 1024, 4096)
+    assert L.nvfp4_linear_segmented_workspace_bytes(0, 16, 64, 8) == 0
+    assert L.nvfp4_linear_segmented_workspace_bytes(1025, 16, 64, 8) == 0
+    for segs in (0, -1, 1025):
+        rc = L.nvfp4_linear_segmented(FAKE, segs, 16, 64, FAKE, FAKE, FAKE, None, 8, 0, FAKE, None, FAKE, 1 << 20, None)
+        assert rc == NVFP4_ERR_ARG and "segments" in _msg()
+    rc = L.nvfp4_linear_segmented(FAKE, 4, -3, 64, FAKE, FAKE, FAKE, None, 8, 0, FAKE, None, FAKE, 1 << 20, None)
+    assert rc == NVFP4_ERR_SHAPE
+    rc = L.nvfp4_quantize_activation_segmented(FAKE, 2, 16, 64, 0, FAKE, FAKE, None, FAKE, 1 << 20, None)
+    assert rc == NVFP4_ERR_ARG                               # the per-segment scales are an output
+    assert L.nvfp4_linear_segmented(None, 3, 0, 64, None, None, None, None, 8, 0, None, None, None, 0, None) == 0
+
+
 def test_empty_input_is_a_no_op():
     assert lib().nvfp4_linear(None, 0, 64, None, None, None, None, 8, None, 0, None, None, 0, None) == 0
     assert lib().nvfp4_quantize_activation(None, 0, 64, None, 0, None, None, None, None, 0, None) == 0

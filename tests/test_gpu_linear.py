@@ -174,3 +174,75 @@ def test_decode_sweep_sampled_columns(name, m):
     r = o.nvfp4_linear_inference(x.float().numpy(), pw, sw, gw, None)
     bound = accumulation_bound(o.dequantize(r["codes"], r["scales"]), o.dequantize(pw, sw), r["alpha"])
     assert_gemm_close(out.float().cpu().numpy()[:, cols], r["out"], bound)
+
+
+def _segmented_inputs(segments, seg_rows, k, seed):
+    """Row blocks with very different magnitudes, so per-segment scales differ."""
+    x = workloads.draw("t3", (segments * seg_rows, k), seed, 0)
+    scale = torch.tensor([2.0 ** (3 * s - 4) * (1.0 + 0.1 * s) for s in range(segments)]).repeat_interleave(seg_rows)
+    return (x.float() * scale[:, None]).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("segments,seg_rows,k,g", [(5, 37, 272, 16), (8, 64, 1024, 0), (3, 1, 96, 2), (16, 130, 512, 128)])
+def test_segmented_quantize_equals_per_segment_calls(segments, seg_rows, k, g):
+    """One global scale per row block: codes, scales and scales bit-identical to quantizing
+    each block alone, and to the oracle."""
+    x = _segmented_inputs(segments, seg_rows, k, segments * 7 + k)
+    codes, scales, gsf = nv().quantize_activation_segmented(x.to(DEV), segments, g)
+    codes_c = codes.cpu().numpy()
+    scales_c = layout_to_canonical(scales.cpu().numpy(), segments * seg_rows, k)
+    for s in range(segments):
+        rows = slice(s * seg_rows, (s + 1) * seg_rows)
+        c1, s1, g1 = nv().quantize_activation(x[rows].to(DEV).contiguous(), None, g)
+        assert np.array_equal(codes_c[rows], c1.cpu().numpy())
+        assert np.array_equal(scales_c[rows], layout_to_canonical(s1.cpu().numpy(), seg_rows, k))
+        assert gsf[s].item() == g1.item()
+        xf = x[rows].float().numpy()
+        if g:
+            xf = o.rotate_activation(xf, g)
+        gx = o.global_sf(o.amax(xf))
+        nib, s8 = o.nvfp4_quantize(xf, gx)
+        assert np.float32(gsf[s].item()) == gx
+        assert np.array_equal(codes_c[rows], o.pack_codes(nib))
+        assert np.array_equal(scales_c[rows], s8)
+
+
+@pytest.mark.parametrize("segments,seg_rows,k,n", [
+    (4, 8, 1024, 1000),      # weight streaming (32 rows)
+    (3, 40, 272, 300),       # K % 32 == 16: register-staged kernel
+    (4, 256, 1024, 1536),    # pipelined kernel, segments aligned to tiles
+    (3, 300, 2048, 4352),    # pipelined kernel, segments crossing tiles, split-K tail
+])
+def test_segmented_linear_per_tile_scales(segments, seg_rows, k, n):
+    """nvfp4_linear_segmented on every GEMM kernel: each row block matches the oracle run
+    on that block alone (its own dynamic scale), and the reported scales are the blocks'."""
+    x = _segmented_inputs(segments, seg_rows, k, n + k)
+    w = workloads.draw("normal", (n, k), 11, n, 0.02)
+    bias = workloads.draw("normal", (n,), 12, n, 0.01)
+    packed, inv_scale, gsf_w = nv().quantize_weight(w.to(DEV))
+    gsf_out = torch.empty((segments,), dtype=torch.float32, device=DEV)
+    out = nv().nvfp4_linear_segmented(x.to(DEV), segments, packed, inv_scale, gsf_w, bias.to(DEV), n, gsf_out=gsf_out)
+    torch.cuda.synchronize()
+    wf = w.float().numpy()
+    pw, sw, gw = o.quantize_weight(wf)
+    got = out.float().cpu().numpy()
+    for s in range(segments):
+        rows = slice(s * seg_rows, (s + 1) * seg_rows)
+        r = o.nvfp4_linear_inference(x[rows].float().numpy(), pw, sw, gw, bias.float().numpy())
+        assert np.float32(gsf_out[s].item()) == r["gsf_x"]
+        bound = accumulation_bound(o.dequantize(r["codes"], r["scales"]), o.dequantize(pw, sw), r["alpha"])
+        assert_gemm_close(got[rows], r["out"], bound)
+
+
+def test_segmented_vit_tiles_match_per_tile_calls():
+    """The ViT decoder tiles (rotation g=16 folded into W, Student-t activations): one
+    segmented pass over 8 tiles against the layer called on each tile alone."""
+    lin = workloads.vit_decoder_tiles(tiles=8, tokens=1024, which=("fc_out",))[0]
+    rows = lin.meta["tile_rows"]
+    layer = nv().NVFP4Linear.from_weight(lin.w.to(DEV), None, rotation_group=lin.rotation_group)
+    x = lin.x.to(DEV)
+    batched = layer.forward_tiles(x, 8)
+    for t in range(8):
+        alone = layer(x[t * rows:(t + 1) * rows])
+        bound = np.full(alone.shape, 0.0, dtype=np.float32)
+        assert_gemm_close(batched[t * rows:(t + 1) * rows].float().cpu().numpy(), alone.float().cpu().numpy(), bound)
