@@ -121,6 +121,26 @@ int nvfp4_quantize_activation(const void* x_dev, int64_t m, int64_t k,
                               void* workspace_dev, size_t workspace_bytes, void* stream);
 
 /*
+ * nvfp4_amax: the activation abs-max the calibration of static scales records ([DEC]
+ * NVFP4DecoderLinear._activation_global_sf while calibrating, calibrate_static_scales):
+ * max |v| over the bf16 [rows][k] input, after the optional rotation (rotation_group
+ * 0 = none; the rotated values are never written).  accumulate 0: *amax_dev = that
+ * maximum; else *amax_dev = max(*amax_dev, it), folding one batch into a running
+ * record.  rows == 0 contributes 0.  workspace >= nvfp4_quantize_workspace_bytes().
+ */
+int nvfp4_amax(const void* x_dev, int64_t rows, int64_t k, int rotation_group, float* amax_dev, int accumulate,
+               void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/*
+ * nvfp4_static_global_scale: the static activation scale of [DEC]
+ * _activation_global_sf from a calibrated abs-max, with calibrate_static_scales'
+ * margin applied to the stored range first: *gsf_dev = fp32(2688 / max(fp32(*amax_dev
+ * * margin), 1e-12)).  margin > 0 (1 = the recorded range as is).  The result is the
+ * global_sf_x argument of nvfp4_linear / nvfp4_quantize_activation for a static scale.
+ */
+int nvfp4_static_global_scale(const float* amax_dev, float margin, float* gsf_dev, void* stream);
+
+/*
  * nvfp4_quantize_activation_segmented: nvfp4_quantize_activation with a dynamic scale
  * applied separately to `segments` consecutive row blocks of seg_rows rows each, as
  * `segments` separate calls would ([TILES]: a dynamic-scale decoder takes one global

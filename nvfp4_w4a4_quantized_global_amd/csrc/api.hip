@@ -219,6 +219,38 @@ int nvfp4_quantize_activation(const void* x, int64_t m, int64_t k, const float* 
                        static_cast<float*>(workspace), static_cast<hipStream_t>(stream));
 }
 
+int nvfp4_amax(const void* x, int64_t rows, int64_t k, int rotation_group, float* amax, int accumulate,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "nvfp4_amax";
+  g_err[0] = 0;
+  if (int rc = check_rows_k(fn, rows, k, true)) return rc;
+  if (int rc = check_group(fn, rotation_group, k, true)) return rc;
+  if (!amax) return fail(NVFP4_ERR_ARG, "%s: amax must not be NULL", fn);
+  if (rows > 0 && !x) return fail(NVFP4_ERR_ARG, "%s: x must not be NULL", fn);
+  if (!workspace || workspace_bytes < nvfp4_quantize_workspace_bytes() ||
+      ((uintptr_t)workspace % NVFP4_WORKSPACE_ALIGN))
+    return fail(NVFP4_ERR_WORKSPACE, "%s: need a %d-byte aligned workspace of %zu bytes", fn, NVFP4_WORKSPACE_ALIGN,
+                nvfp4_quantize_workspace_bytes());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* partials = static_cast<float*>(workspace);
+  int n_partials = 0;
+  if (rows > 0) {
+    int rc = hip_status(nvfp4::launch_amax_partials(static_cast<const uint16_t*>(x), rows, k, 1, rotation_group,
+                                                    inv_sqrt(rotation_group), partials, &n_partials, s), fn);
+    if (rc) return rc;
+  }
+  return hip_status(nvfp4::launch_amax_finalize(partials, n_partials, amax, accumulate != 0, s), fn);
+}
+
+int nvfp4_static_global_scale(const float* amax, float margin, float* gsf, void* stream) {
+  const char* fn = "nvfp4_static_global_scale";
+  g_err[0] = 0;
+  if (!amax || !gsf) return fail(NVFP4_ERR_ARG, "%s: NULL argument", fn);
+  if (!(margin > 0.0f) || margin != margin || margin > 3.0e38f)
+    return fail(NVFP4_ERR_ARG, "%s: margin must be a positive finite number", fn);
+  return hip_status(nvfp4::launch_static_scale(amax, margin, gsf, static_cast<hipStream_t>(stream)), fn);
+}
+
 int nvfp4_quantize_activation_segmented(const void* x, int64_t segments, int64_t seg_rows, int64_t k,
                                         int rotation_group, uint8_t* codes, uint8_t* scales, float* gsf_out,
                                         void* workspace, size_t workspace_bytes, void* stream) {

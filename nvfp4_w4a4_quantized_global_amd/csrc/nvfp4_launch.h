@@ -23,6 +23,12 @@ hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t k, int group
                            const float* static_gsf, const float* partials, int n_partials, int64_t seg_rows,
                            int segments, uint8_t* codes, uint8_t* scales, float* gsf_out, hipStream_t s);
 
+// *amax = max of n_partials partial maxima (accumulate: max with the value already there).
+hipError_t launch_amax_finalize(const float* partials, int n_partials, float* amax, bool accumulate, hipStream_t s);
+
+// *gsf = 2688 / max(fp32(*amax * margin), 1e-12).
+hipError_t launch_static_scale(const float* amax, float margin, float* gsf, hipStream_t s);
+
 hipError_t launch_rotate(const void* x, bool x_bf16, void* y, bool y_bf16, int64_t rows, int64_t k, int group,
                          float inv_sqrt_g, hipStream_t s);
 

@@ -194,6 +194,23 @@ __global__ void __launch_bounds__(kThreads) quantize_kernel(
   }
 }
 
+// Calibration: *amax = max over the partial maxima, or max(*amax, that) when
+// accumulating over batches.
+__global__ void __launch_bounds__(kThreads) amax_finalize_kernel(const float* __restrict__ partials, int n_partials,
+                                                                  float* __restrict__ amax, int accumulate) {
+  __shared__ float lds[kThreads / 64];
+  float a = 0.0f;
+  for (int i = threadIdx.x; i < n_partials; i += kThreads) a = fmaxf(a, partials[i]);
+  a = block_max(a, lds);
+  if (threadIdx.x == 0) *amax = accumulate ? fmaxf(*amax, a) : a;
+}
+
+// Static activation scale from a calibrated amax: the stored range is fp32(amax *
+// margin) and the scale 2688 / max(range, 1e-12), both in fp32.
+__global__ void static_scale_kernel(const float* __restrict__ amax, float margin, float* __restrict__ gsf) {
+  if (threadIdx.x == 0) *gsf = global_scale_from_amax(__fmul_rn(*amax, margin));
+}
+
 // Stand-alone rotation: x (bf16 or fp32) -> y (bf16 or fp32), one 16-value chunk per lane.
 template <typename Tin, bool kOutBf16>
 __global__ void __launch_bounds__(kThreads) rotate_kernel(const Tin* __restrict__ x, void* __restrict__ y,
@@ -289,6 +306,16 @@ hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t k, int group
   else
     hipLaunchKernelGGL(quantize_kernel<false>, dim3((uint32_t)grid), dim3(kThreads), 0, s, x, rows, k, group, inv_sqrt_g,
                        static_gsf, partials, n_partials, seg_rows, segments, codes, scales, gsf_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax_finalize(const float* partials, int n_partials, float* amax, bool accumulate, hipStream_t s) {
+  hipLaunchKernelGGL(amax_finalize_kernel, dim3(1), dim3(kThreads), 0, s, partials, n_partials, amax, (int)accumulate);
+  return hipGetLastError();
+}
+
+hipError_t launch_static_scale(const float* amax, float margin, float* gsf, hipStream_t s) {
+  hipLaunchKernelGGL(static_scale_kernel, dim3(1), dim3(64), 0, s, amax, margin, gsf);
   return hipGetLastError();
 }
 

@@ -204,6 +204,36 @@ def nvfp4_linear(x: torch.Tensor, packed: torch.Tensor, inv_scale: torch.Tensor,
     return out.reshape(*orig[:-1], out_features)
 
 
+def amax(x: torch.Tensor, rotation_group: int = 0, out: torch.Tensor | None = None,
+         accumulate: bool = False) -> torch.Tensor:
+    """max |x| over a bf16 [.., K] input after the optional block rotation, as an fp32 0-d
+    device tensor; with ``accumulate`` the running value in ``out`` is raised instead."""
+    if x.dtype != torch.bfloat16:
+        raise ValueError(f"x must be bf16, got {x.dtype}")
+    k = x.shape[-1]
+    x2d = x.reshape(-1, k)
+    if not x2d.is_contiguous():
+        x2d = x2d.contiguous()
+    _require_cuda("x", x2d, torch.bfloat16, 2)
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs the running value in out")
+        out = torch.empty((), dtype=torch.float32, device=x.device)
+    _require_cuda("out", out, torch.float32)
+    ws = torch.empty((quantize_workspace_bytes(),), dtype=torch.uint8, device=x.device)
+    check(lib().nvfp4_amax(_ptr(x2d), x2d.shape[0], k, int(rotation_group), _ptr(out), int(bool(accumulate)), _ptr(ws),
+                           ws.numel(), _stream(x.device)))
+    return out
+
+
+def static_global_sf(input_amax: torch.Tensor, margin: float = 1.0) -> torch.Tensor:
+    """Static activation scale 2688 / max(fp32(input_amax * margin), 1e-12) (fp32 0-d)."""
+    _require_cuda("input_amax", input_amax, torch.float32)
+    gsf = torch.empty((), dtype=torch.float32, device=input_amax.device)
+    check(lib().nvfp4_static_global_scale(_ptr(input_amax), float(margin), _ptr(gsf), _stream(input_amax.device)))
+    return gsf
+
+
 def _segment_rows(x2d: torch.Tensor, segments: int) -> int:
     if not 1 <= int(segments) <= 1024:
         raise ValueError(f"segments must be in [1, 1024], got {segments}")
@@ -303,7 +333,7 @@ class NVFP4Linear:
     ACT_SCALES = ("dynamic", "static", "unit")
 
     def __init__(self, packed, inv_scale, global_sf_w, bias, in_features, rotation_group=None,
-                 act_scale="dynamic", input_amax=None):
+                 act_scale="dynamic", input_amax=None, margin: float = 1.0):
         if in_features % NVFP4_BLOCK_SIZE:
             raise ValueError(f"NVFP4 needs in_features divisible by {NVFP4_BLOCK_SIZE}, got {in_features}")
         if rotation_group is not None and in_features % rotation_group:
@@ -320,6 +350,8 @@ class NVFP4Linear:
         self.rotation_group = rotation_group
         self.act_scale = act_scale
         self.input_amax = input_amax
+        self.margin = float(margin)
+        self.calibrating = False
         self._gsf_x = None
 
     @classmethod
@@ -348,20 +380,56 @@ class NVFP4Linear:
             else:
                 if self.input_amax is None:
                     raise ValueError("act_scale='static' needs input_amax")
-                amax = torch.as_tensor(self.input_amax, dtype=torch.float32, device=self.packed.device)
-                # 2688 / amax.clamp(min=1e-12) in fp32; computed once on the device by torch
-                self._gsf_x = torch.tensor(2688.0, dtype=torch.float32, device=amax.device) / amax.clamp(min=1e-12)
+                amax_t = torch.as_tensor(self.input_amax, dtype=torch.float32, device=self.packed.device).reshape(())
+                self._gsf_x = static_global_sf(amax_t.contiguous(), self.margin)
         return self._gsf_x
 
+    # Calibration of a static scale ("minimax_h3_nvfp4_decoder" page,
+    # calibrate_static_scales): record the running abs-max of the (rotated) inputs
+    # while running with dynamic numerics, then switch to the static scale.
+    def start_calibration(self) -> None:
+        self._record = torch.zeros((), dtype=torch.float32, device=self.packed.device)
+        self.calibrating = True
+
+    def finish_calibration(self, margin: float = 1.0) -> None:
+        self.calibrating = False
+        if not float(self._record.item()) > 0.0:
+            raise RuntimeError("an NVFP4 linear saw no activations during calibration")
+        self.input_amax, self.margin, self.act_scale, self._gsf_x = self._record, float(margin), "static", None
+
     def __call__(self, x: torch.Tensor) -> torch.Tensor:
-        return nvfp4_linear(x.to(torch.bfloat16), self.packed, self.inv_scale, self.global_sf_w, self.bias,
+        x = x.to(torch.bfloat16)
+        if self.calibrating:
+            amax(x, self.rotation_group or 0, out=self._record, accumulate=True)
+            return nvfp4_linear(x, self.packed, self.inv_scale, self.global_sf_w, self.bias, self.out_features, None,
+                                self.rotation_group or 0)
+        return nvfp4_linear(x, self.packed, self.inv_scale, self.global_sf_w, self.bias,
                             self.out_features, self.activation_global_sf(), self.rotation_group or 0)
 
     def forward_tiles(self, x: torch.Tensor, tiles: int) -> torch.Tensor:
         """x holds ``tiles`` equal row blocks (decoder tiles); one pass over all of them
         with the result of calling the layer on each tile alone.  With a dynamic scale
         every tile keeps its own global scale; static and unit scales are shared anyway."""
+        if self.calibrating:
+            return self(x)
         if self.act_scale != "dynamic":
             return self(x)
         return nvfp4_linear_segmented(x.to(torch.bfloat16), tiles, self.packed, self.inv_scale, self.global_sf_w,
                                       self.bias, self.out_features, self.rotation_group or 0)
+
+
+def calibrate_static_scales(layers, run_batches, margin: float = 1.0) -> int:
+    """Record every layer's activation abs-max over ``run_batches()`` (dynamic numerics
+    while recording), then switch the layers to static scales with ``margin`` applied
+    to the recorded range; returns the number of layers."""
+    layers = list(layers)
+    for layer in layers:
+        layer.start_calibration()
+    try:
+        run_batches()
+    finally:
+        for layer in layers:
+            layer.calibrating = False
+    for layer in layers:
+        layer.finish_calibration(margin)
+    return len(layers)

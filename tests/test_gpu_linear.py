@@ -246,3 +246,48 @@ def test_segmented_vit_tiles_match_per_tile_calls():
         alone = layer(x[t * rows:(t + 1) * rows])
         bound = np.full(alone.shape, 0.0, dtype=np.float32)
         assert_gemm_close(batched[t * rows:(t + 1) * rows].float().cpu().numpy(), alone.float().cpu().numpy(), bound)
+
+
+@pytest.mark.parametrize("rows,k,g", [(1, 16, 0), (37, 272, 16), (300, 1024, 0), (64, 512, 128)])
+def test_amax_and_accumulate(rows, k, g):
+    """Calibration abs-max of the (rotated) input: exact against the oracle; the
+    accumulating form keeps the running maximum over batches."""
+    xs = [workloads.draw("t3", (rows, k), rows + k, i, 1.0 + i) for i in range(3)]
+    ref = []
+    for x in xs:
+        xf = x.float().numpy()
+        ref.append(o.amax(o.rotate_activation(xf, g) if g else xf))
+    first = nv().amax(xs[0].to(DEV), g)
+    assert np.float32(first.item()) == np.float32(ref[0])
+    running = torch.zeros((), dtype=torch.float32, device=DEV)
+    for x in xs:
+        nv().amax(x.to(DEV), g, out=running, accumulate=True)
+    assert np.float32(running.item()) == np.float32(max(ref))
+
+
+@pytest.mark.parametrize("amax", [0.0, 1e-13, 3.0e-5, 25.0, 448.0, 1.0e30])
+@pytest.mark.parametrize("margin", [1.0, 1.25, 0.5])
+def test_static_global_scale(amax, margin):
+    a = torch.tensor(amax, dtype=torch.float32, device=DEV)
+    got = np.float32(nv().static_global_sf(a, margin).item())
+    assert got == o.global_sf(np.float32(np.float32(amax) * np.float32(margin)))
+
+
+def test_calibration_then_static_forward():
+    """calibrate_static_scales over three batches (rotation 16, margin 1.5): the static
+    scale is 2688 / (largest recorded abs-max * 1.5), and the static forward matches the
+    oracle run with that scale."""
+    lin = workloads.vit_decoder_tiles(tiles=3, tokens=256, which=("qkv",))[0]
+    rows = lin.meta["tile_rows"]
+    g = lin.rotation_group
+    layer = nv().NVFP4Linear.from_weight(lin.w.to(DEV), None, rotation_group=g)
+    x = lin.x.to(DEV)
+    n = nv().calibrate_static_scales([layer], lambda: [layer(x[t * rows:(t + 1) * rows]) for t in range(3)], 1.5)
+    assert n == 1 and layer.act_scale == "static"
+    xf = lin.x.float().numpy()
+    recorded = max(o.amax(o.rotate_activation(xf[t * rows:(t + 1) * rows], g)) for t in range(3))
+    gx = o.global_sf(np.float32(np.float32(recorded) * np.float32(1.5)))
+    assert np.float32(layer.activation_global_sf().item()) == gx
+    tile = x[:rows]
+    out = layer(tile)
+    check_against_oracle(lin, lin.x[:rows], out, layer.packed, layer.inv_scale, layer.global_sf_w, gx, g)
