@@ -205,6 +205,17 @@ int nvfp4_linear_segmented(const void* x_dev, int64_t segments, int64_t seg_rows
                            int rotation_group, void* out_dev, float* gsf_out_dev,
                            void* workspace_dev, size_t workspace_bytes, void* stream);
 
+/*
+ * nvfp4_dequantize: NVFP4 back to real values, the expansion the fused-dequant
+ * fallback performs on GPUs that run the linear as a 16-bit GEMM ([TILES] the
+ * encoder's fused dequantization flag).  out[r][i] = fp32(code * scale) / global_sf
+ * (IEEE fp32), stored as bf16 (nearest even) or fp32 per out_dtype (NVFP4_DTYPE_*).
+ * packed_dev [rows][k/2] (8-byte aligned), scale_dev (layout above), global_sf_dev
+ * the tensor's fp32 scale, out_dev [rows][k] (16-byte aligned).
+ */
+int nvfp4_dequantize(const uint8_t* packed_dev, const uint8_t* scale_dev, int64_t rows, int64_t k,
+                     const float* global_sf_dev, void* out_dev, int out_dtype, void* stream);
+
 /* Scale-layout conversion: layout above <-> row-major [rows][k/16] bytes. */
 int nvfp4_scale_to_canonical(const uint8_t* layout_dev, uint8_t* canonical_dev,
                              int64_t rows, int64_t k, void* stream);

@@ -35,6 +35,7 @@ SIGNATURES = {
     "rotate_activation": (_int, [_vp, _int, _vp, _int, _i64, _i64, _int, _vp]),
     "nvfp4_quantize_weight": (_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_quantize_activation": (_int, [_vp, _i64, _i64, _vp, _int, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "nvfp4_dequantize": (_int, [_vp, _vp, _i64, _i64, _vp, _vp, _int, _vp]),
     "nvfp4_amax": (_int, [_vp, _i64, _i64, _int, _vp, _int, _vp, _sz, _vp]),
     "nvfp4_static_global_scale": (_int, [_vp, ctypes.c_float, _vp, _vp]),
     "nvfp4_quantize_activation_segmented": (_int, [_vp, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _sz, _vp]),

@@ -242,6 +242,22 @@ int nvfp4_amax(const void* x, int64_t rows, int64_t k, int rotation_group, float
   return hip_status(nvfp4::launch_amax_finalize(partials, n_partials, amax, accumulate != 0, s), fn);
 }
 
+int nvfp4_dequantize(const uint8_t* packed, const uint8_t* scales, int64_t rows, int64_t k, const float* global_sf,
+                     void* out, int out_dtype, void* stream) {
+  const char* fn = "nvfp4_dequantize";
+  g_err[0] = 0;
+  if (int rc = check_rows_k(fn, rows, k, true)) return rc;
+  if (out_dtype != NVFP4_DTYPE_BF16 && out_dtype != NVFP4_DTYPE_F32)
+    return fail(NVFP4_ERR_ARG, "%s: out_dtype must be NVFP4_DTYPE_BF16 or NVFP4_DTYPE_F32", fn);
+  if (rows == 0) return NVFP4_OK;
+  if (!packed || !scales || !global_sf || !out) return fail(NVFP4_ERR_ARG, "%s: NULL argument", fn);
+  if (((uintptr_t)packed % 8) || ((uintptr_t)out % 16))
+    return fail(NVFP4_ERR_ARG, "%s: packed must be 8-byte and out 16-byte aligned", fn);
+  return hip_status(nvfp4::launch_dequant(packed, scales, rows, k, global_sf, out, out_dtype == NVFP4_DTYPE_BF16,
+                                          static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 int nvfp4_static_global_scale(const float* amax, float margin, float* gsf, void* stream) {
   const char* fn = "nvfp4_static_global_scale";
   g_err[0] = 0;

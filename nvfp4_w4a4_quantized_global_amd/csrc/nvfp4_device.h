@@ -44,6 +44,14 @@ __device__ __forceinline__ float e4m3_decode(uint32_t b) {
   return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
 }
 
+// E2M1 nibble -> fp32, exact: magnitudes 0, .5, 1, 1.5 for codes 0-3, then
+// 2^(e-1) * (1 + m/2) for codes 4-7 (e = code >> 1, m = code & 1); bit 3 is the sign.
+__device__ __forceinline__ float e2m1_decode(uint32_t c) {
+  const uint32_t mag = c & 7u;
+  const float a = mag < 4u ? 0.5f * (float)mag : __uint_as_float(((126u + (mag >> 1)) << 23) | ((mag & 1u) << 22));
+  return (c & 8u) ? -a : a;
+}
+
 // fp32 -> E2M1 nibble, nearest even, saturating at 6; the sign bit of v is kept.
 // Below 1 the grid is uniform (step 0.5), so the magnitude code is rint(2|v|);
 // from 1 up, the fp32 significand is rounded to one bit and the exponent rebiased

@@ -23,6 +23,11 @@ hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t k, int group
                            const float* static_gsf, const float* partials, int n_partials, int64_t seg_rows,
                            int segments, uint8_t* codes, uint8_t* scales, float* gsf_out, hipStream_t s);
 
+// NVFP4 [rows][k] (codes + scales in the library layout) -> bf16 or fp32 values
+// fp32(code * scale) / gsf.
+hipError_t launch_dequant(const uint8_t* packed, const uint8_t* scales, int64_t rows, int64_t k, const float* gsf,
+                          void* out, bool out_bf16, hipStream_t s);
+
 // *amax = max of n_partials partial maxima (accumulate: max with the value already there).
 hipError_t launch_amax_finalize(const float* partials, int n_partials, float* amax, bool accumulate, hipStream_t s);
 

@@ -194,6 +194,39 @@ __global__ void __launch_bounds__(kThreads) quantize_kernel(
   }
 }
 
+// NVFP4 -> real values: each 16-block fp32(code * scale) / gsf, stored as bf16 (RNE) or
+// fp32.  One lane per block: 8 code bytes in, 32 or 64 bytes out.
+template <bool kOutBf16>
+__global__ void __launch_bounds__(kThreads) dequant_kernel(const uint8_t* __restrict__ packed,
+                                                            const uint8_t* __restrict__ scales, int64_t rows, int64_t k,
+                                                            const float* __restrict__ gsf, void* __restrict__ out) {
+  const int64_t nb = k / kBlock;
+  const int64_t blocks = rows * nb;
+  const float g = *gsf;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < blocks; b += stride) {
+    const int64_t r = b / nb, j = b - r * nb;
+    const uint2 c = *reinterpret_cast<const uint2*>(packed + r * (k / 2) + j * 8);
+    const float s = e4m3_decode(scales[((j >> 3) * rows + r) * 8 + (j & 7)]);
+    const uint32_t w[2] = {c.x, c.y};
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = __fdiv_rn(__fmul_rn(e2m1_decode((w[i >> 3] >> (4 * (i & 7))) & 0xFu), s), g);
+    if (kOutBf16) {
+      uint32_t o[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = f32_to_bf16(v[2 * i]) | (f32_to_bf16(v[2 * i + 1]) << 16);
+      uint4* d = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + r * k + j * kBlock);
+      d[0] = make_uint4(o[0], o[1], o[2], o[3]);
+      d[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    } else {
+      float4* d = reinterpret_cast<float4*>(static_cast<float*>(out) + r * k + j * kBlock);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+    }
+  }
+}
+
 // Calibration: *amax = max over the partial maxima, or max(*amax, that) when
 // accumulating over batches.
 __global__ void __launch_bounds__(kThreads) amax_finalize_kernel(const float* __restrict__ partials, int n_partials,
@@ -306,6 +339,16 @@ hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t k, int group
   else
     hipLaunchKernelGGL(quantize_kernel<false>, dim3((uint32_t)grid), dim3(kThreads), 0, s, x, rows, k, group, inv_sqrt_g,
                        static_gsf, partials, n_partials, seg_rows, segments, codes, scales, gsf_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const uint8_t* packed, const uint8_t* scales, int64_t rows, int64_t k, const float* gsf,
+                          void* out, bool out_bf16, hipStream_t s) {
+  const int grid = (int)grid_for(rows * (k / kBlock), 8192);
+  if (out_bf16)
+    hipLaunchKernelGGL(dequant_kernel<true>, dim3(grid), dim3(kThreads), 0, s, packed, scales, rows, k, gsf, out);
+  else
+    hipLaunchKernelGGL(dequant_kernel<false>, dim3(grid), dim3(kThreads), 0, s, packed, scales, rows, k, gsf, out);
   return hipGetLastError();
 }
 

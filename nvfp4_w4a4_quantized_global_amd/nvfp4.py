@@ -226,6 +226,25 @@ def amax(x: torch.Tensor, rotation_group: int = 0, out: torch.Tensor | None = No
     return out
 
 
+def dequantize(packed: torch.Tensor, scales: torch.Tensor, global_sf, dtype: torch.dtype = torch.bfloat16
+               ) -> torch.Tensor:
+    """NVFP4 [rows, K/2] + scales back to ``dtype`` values fp32(code * scale) / global_sf."""
+    _require_cuda("packed", packed, torch.uint8, 2)
+    _require_cuda("scales", scales, torch.uint8)
+    codes = {torch.bfloat16: _lib.NVFP4_DTYPE_BF16, torch.float32: _lib.NVFP4_DTYPE_F32}
+    if dtype not in codes:
+        raise ValueError(f"dequantize supports bf16 and fp32 outputs, got {dtype}")
+    rows, half_k = packed.shape
+    k = 2 * half_k
+    if scales.numel() < scale_bytes(rows, k):
+        raise ValueError("scales is smaller than nvfp4_scale_bytes(rows, K)")
+    g = _scalar_f32(global_sf, packed.device)
+    out = torch.empty((rows, k), dtype=dtype, device=packed.device)
+    check(lib().nvfp4_dequantize(_ptr(packed), _ptr(scales), rows, k, _ptr(g), _ptr(out), codes[dtype],
+                                 _stream(packed.device)))
+    return out
+
+
 def static_global_sf(input_amax: torch.Tensor, margin: float = 1.0) -> torch.Tensor:
     """Static activation scale 2688 / max(fp32(input_amax * margin), 1e-12) (fp32 0-d)."""
     _require_cuda("input_amax", input_amax, torch.float32)
@@ -405,6 +424,10 @@ class NVFP4Linear:
                                 self.rotation_group or 0)
         return nvfp4_linear(x, self.packed, self.inv_scale, self.global_sf_w, self.bias,
                             self.out_features, self.activation_global_sf(), self.rotation_group or 0)
+
+    def dequantized_weight(self, dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+        """The packed weight expanded back to ``dtype`` (the W4A16 fallback's weight)."""
+        return dequantize(self.packed, self.inv_scale, self.global_sf_w, dtype)
 
     def forward_tiles(self, x: torch.Tensor, tiles: int) -> torch.Tensor:
         """x holds ``tiles`` equal row blocks (decoder tiles); one pass over all of them

@@ -16,6 +16,9 @@ Pages cited by title:
   ``forward``).
 * [CONV] "convert_minimax_h3_text_encoder_nvfp4.py" (checkpoint conversion
   script): module docstring, ``probe_relative_error``, ``main``.
+* [TILES] "[bugfix]: decode dynamic-scale NVFP4 H3 VAE tiles one at a time"
+  (diff of the decoder's tile batching and environment flags): the fused
+  dequantization flag of the encoder.
 * [BLOG] "FastH3-QAD-v2 and NVFP4 VAE Decoders: Better Quality, Faster
   Decoding, and Community LoRAs": sections "Fused FP4 kernels" and "The whole
   stack in NVFP4".
@@ -64,7 +67,7 @@ __all__ = [
     "FP4_E4M3_RANGE", "NVFP4_BLOCK_SIZE", "E2M1_MAGNITUDES", "e2m1_decode", "e2m1_encode",
     "e4m3_decode", "e4m3_encode", "E4M3_VALUES", "AMAX_FLOOR", "bf16_round", "bf16_bits_to_f32", "f32_to_bf16_bits",
     "sylvester_hadamard", "fwht_f32", "rotate_activation", "fold_weight", "amax", "global_sf",
-    "nvfp4_quantize", "pack_codes", "unpack_codes", "dequantize", "quantize_weight",
+    "nvfp4_quantize", "pack_codes", "unpack_codes", "dequantize", "dequantize_values", "quantize_weight",
     "alpha_of", "nvfp4_gemm", "nvfp4_linear_inference", "probe_relative_error",
 ]
 
@@ -284,6 +287,16 @@ def dequantize(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
     rows, k = vals.shape
     s = e4m3_decode(scales)
     return (vals.reshape(rows, k // 16, 16) * s[:, :, None]).reshape(rows, k)
+
+
+def dequantize_values(packed: np.ndarray, scales: np.ndarray, gsf, out: str = "bf16") -> np.ndarray:
+    """NVFP4 back to real values, the fused-dequant fallback's expansion of a weight
+    ([TILES] the encoder expanded in one pass on GPUs without an FP4 GEMM): each
+    value fp32(code * scale) divided by the global scale in fp32, then rounded to bf16
+    (``out='bf16'``) or kept in fp32 (``out='f32'``)."""
+    prod = dequantize(packed, scales).astype(np.float32)          # exact
+    v = (prod / np.float32(gsf)).astype(np.float32)
+    return bf16_round(v) if out == "bf16" else v
 
 
 def quantize_weight(w_values: np.ndarray) -> tuple[np.ndarray, np.ndarray, np.float32]:

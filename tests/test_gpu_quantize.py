@@ -6,7 +6,7 @@ import torch
 
 import oracle as o
 import workloads
-from tests._util import layout_padding, layout_to_canonical, oracle_quantize
+from tests._util import canonical_to_layout, layout_padding, layout_to_canonical, oracle_quantize
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -151,3 +151,32 @@ def test_small_m_bitwise(m):
         if lin.name.endswith(("k_proj", "up_proj")):     # same K as v/gate; keep the sweep short
             continue
         assert_same(gpu_quantize(lin.x), oracle_expected(lin.x), lin.name)
+
+
+@pytest.mark.parametrize("rows,k", [(1, 16), (37, 272), (300, 1024), (5, 4112)])
+@pytest.mark.parametrize("gsf", [1.0, 8.0, 2688.0 / 3.7, 1.0e-3])
+def test_dequantize_bitwise(rows, k, gsf):
+    """NVFP4 -> bf16 / fp32 expansion bit-exact against the oracle over every E4M3 byte
+    (subnormal and zero scales included) and signed zero codes."""
+    rng = np.random.default_rng(rows + k)
+    nib = rng.integers(0, 16, size=(rows, k), dtype=np.uint8)
+    s8 = rng.integers(0, 127, size=(rows, k // 16)).astype(np.uint8)
+    packed = o.pack_codes(nib)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    lay = t(canonical_to_layout(s8, k))
+    g = np.float32(gsf)
+    for dtype, mode in ((torch.bfloat16, "bf16"), (torch.float32, "f32")):
+        got = nv().dequantize(t(packed), lay, float(g), dtype)
+        ref = o.dequantize_values(packed, s8, g, out=mode)
+        if dtype == torch.bfloat16:
+            assert np.array_equal(got.view(torch.int16).cpu().numpy().view(np.uint16), o.f32_to_bf16_bits(ref))
+        else:
+            assert np.array_equal(got.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+def test_dequantized_weight_of_a_layer():
+    lin = workloads.tiny_linear()
+    layer = nv().NVFP4Linear.from_weight(lin.w.to(DEV))
+    pw, sw, gw = o.quantize_weight(lin.w.float().numpy())
+    got = layer.dequantized_weight().float().cpu().numpy()
+    assert np.array_equal(got, o.dequantize_values(pw, sw, gw))

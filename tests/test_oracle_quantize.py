@@ -107,3 +107,30 @@ def test_pack_unpack_round_trip():
 def test_quantizer_rejects_bad_k():
     with pytest.raises(ValueError):
         o.nvfp4_quantize(np.zeros((2, 24), dtype=np.float32), 1.0)
+
+
+def test_dequantize_values_pins():
+    """Expansion back to real values: with a power-of-two global scale the division is
+    exact (codes * scale * 2^-k, checked against a bit-level decode of each field);
+    for any scale, quantize-then-expand stays within half an E2M1 step of the block
+    (the quantisation bound) plus the final bf16 rounding."""
+    rng = np.random.default_rng(5)
+    nib = rng.integers(0, 16, size=(7, 64), dtype=np.uint8)
+    s8 = rng.integers(1, 127, size=(7, 4)).astype(np.uint8)
+    packed = o.pack_codes(nib)
+    got = o.dequantize_values(packed, s8, np.float32(8.0), out="f32")
+    mag = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    e, mnt = (s8 >> 3).astype(np.int64), (s8 & 7).astype(np.float64)
+    sv = np.where(e == 0, mnt / 8 * 2.0 ** -6, (1 + mnt / 8) * 2.0 ** (e - 7))
+    want = (np.where(nib >> 3, -1.0, 1.0) * mag[nib & 7]).reshape(7, 4, 16) * sv[:, :, None] / 8.0
+    assert np.array_equal(got, want.reshape(7, 64).astype(np.float32))
+    # round trip on real data
+    x = rng.standard_normal((33, 256)).astype(np.float32) * 3
+    gsf = o.global_sf(o.amax(x))
+    nib2, s82 = o.nvfp4_quantize(x, gsf)
+    back = o.dequantize_values(o.pack_codes(nib2), s82, gsf, out="f32")
+    step_half = 1.0 * o.e4m3_decode(s82).astype(np.float64) / float(gsf)      # half the widest E2M1 step (2)
+    err = np.abs(back - x).reshape(33, 16, 16).max(axis=2)
+    assert np.all(err <= step_half * (1 + 1e-6))
+    b16 = o.dequantize_values(o.pack_codes(nib2), s82, gsf)
+    assert np.array_equal(b16, o.bf16_round(back))
