@@ -68,7 +68,7 @@ __all__ = [
     "e4m3_decode", "e4m3_encode", "E4M3_VALUES", "AMAX_FLOOR", "bf16_round", "bf16_bits_to_f32", "f32_to_bf16_bits",
     "sylvester_hadamard", "fwht_f32", "rotate_activation", "fold_weight", "amax", "global_sf",
     "nvfp4_quantize", "pack_codes", "unpack_codes", "dequantize", "dequantize_values", "quantize_weight",
-    "alpha_of", "nvfp4_gemm", "nvfp4_linear_inference", "probe_relative_error",
+    "alpha_of", "nvfp4_gemm", "nvfp4_linear_inference", "probe_relative_error", "exp_f32", "swiglu_product",
 ]
 
 # ---------------------------------------------------------------------------
@@ -297,6 +297,42 @@ def dequantize_values(packed: np.ndarray, scales: np.ndarray, gsf, out: str = "b
     prod = dequantize(packed, scales).astype(np.float32)          # exact
     v = (prod / np.float32(gsf)).astype(np.float32)
     return bf16_round(v) if out == "bf16" else v
+
+
+# ---------------------------------------------------------------------------
+# SwiGLU product that feeds down_proj ([CONV] module docstring: that product carries
+# the widest activation outliers of the layer).  The pages do not print its
+# numerics; the reading taken is x = bf16(fp32(fp32(g / fp32(1 + exp(-g))) * u)), with
+# exp evaluated in fp32 by Cody-Waite reduction t = n*ln2 + r (ln2 split into a
+# 15-bit head and a tail, so n*head is exact), a degree-6 Taylor polynomial for e^r in
+# Horner form and an exact scaling by 2^n.  Every step is one IEEE fp32 operation.
+# ---------------------------------------------------------------------------
+_F = np.float32
+EXP_CLAMP = _F(80.0)
+EXP_LOG2E = _F(float.fromhex("0x1.715476p+0"))
+EXP_LN2_HI = _F(float.fromhex("0x1.62e4p-1"))
+EXP_LN2_LO = _F(float.fromhex("0x1.7f7d1cp-20"))
+EXP_TAYLOR = tuple(_F(1.0 / math.factorial(i)) for i in range(7))   # 1, 1, 1/2, ..., 1/720 in fp32
+
+
+def exp_f32(t: np.ndarray) -> np.ndarray:
+    """exp(t) for fp32 t, clamped to [-80, 80], by the steps above."""
+    t = np.clip(np.asarray(t, dtype=np.float32), -EXP_CLAMP, EXP_CLAMP)
+    n = np.rint(t * EXP_LOG2E).astype(np.float32)
+    r = ((t - n * EXP_LN2_HI).astype(np.float32) - n * EXP_LN2_LO).astype(np.float32)
+    p = EXP_TAYLOR[6]
+    for c in EXP_TAYLOR[5::-1]:
+        p = (p * r).astype(np.float32) + c
+        p = np.asarray(p, dtype=np.float32)
+    return np.ldexp(p, n.astype(np.int32)).astype(np.float32)
+
+
+def swiglu_product(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """bf16-rounded silu(g) * u (returned as float32 values), g and u bf16 values."""
+    g = np.asarray(g, dtype=np.float32)
+    u = np.asarray(u, dtype=np.float32)
+    d = (np.float32(1.0) + exp_f32(-g)).astype(np.float32)
+    return bf16_round(((g / d).astype(np.float32) * u).astype(np.float32))
 
 
 def quantize_weight(w_values: np.ndarray) -> tuple[np.ndarray, np.ndarray, np.float32]:
