@@ -62,6 +62,10 @@ enum { NVFP4_DTYPE_BF16 = 0, NVFP4_DTYPE_F32 = 1 };
 #define NVFP4_MAX_ROTATION_GROUP 128
 #define NVFP4_WORKSPACE_ALIGN 256
 
+/* Every bf16 / fp32 activation, weight or output tensor passed to the library must
+ * be 16-byte aligned (misaligned pointers are rejected with NVFP4_ERR_ARG); packed
+ * codes and scales follow the alignment each call states. */
+
 /* Bytes of a block-scale array for a [rows, k] tensor in the layout above. */
 size_t nvfp4_scale_bytes(int64_t rows, int64_t k);
 
@@ -204,6 +208,48 @@ int nvfp4_linear_segmented(const void* x_dev, int64_t segments, int64_t seg_rows
                            const float* global_sf_w_dev, const void* bias_dev, int64_t out_features,
                            int rotation_group, void* out_dev, float* gsf_out_dev,
                            void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/*
+ * nvfp4_swiglu: the SwiGLU product that feeds down_proj ([CONV] module docstring: it
+ * carries the widest activation outliers of the layer; --keep-bf16 mlp.down_proj).
+ * x[r][i] = bf16(fp32(fp32(g / fp32(1 + exp(-g))) * u)) for g = gate[r][i], u =
+ * up[r][i], with exp evaluated in fp32 by Cody-Waite reduction (15-bit ln2 head),
+ * a degree-6 Taylor polynomial and an exact 2^n scaling, on an argument clamped to
+ * [-80, 80] (within 3 ulps of exp; the steps fix the result bit for bit).
+ * gate_dev, up_dev, x_dev: bf16 [rows][k], 16-byte aligned.
+ */
+int nvfp4_swiglu(const void* gate_dev, const void* up_dev, int64_t rows, int64_t k, void* x_dev, void* stream);
+
+/* Workspaces of nvfp4_quantize_swiglu and nvfp4_linear_swiglu with a dynamic scale:
+ * the plain ones plus room for the [m][k] bf16 product, which the amax pass forms once
+ * and the quantize pass reads (a static scale needs no room: its single pass forms
+ * the product in registers). */
+size_t nvfp4_quantize_swiglu_workspace_bytes(int64_t m, int64_t k);
+size_t nvfp4_linear_swiglu_workspace_bytes(int64_t m, int64_t k, int64_t n);
+
+/*
+ * nvfp4_quantize_swiglu: nvfp4_quantize_activation (no rotation) of
+ * nvfp4_swiglu(gate, up) in fewer passes: the same codes, scales and global scale.
+ * A static scale (global_sf_x_dev not NULL) quantizes in one pass that forms the
+ * product in registers and writes only codes and scales; a dynamic one forms the
+ * product in the amax pass (into the workspace) and quantizes it from there, saving
+ * the separate SwiGLU pass.  workspace: >= nvfp4_quantize_swiglu_workspace_bytes.
+ */
+int nvfp4_quantize_swiglu(const void* gate_dev, const void* up_dev, int64_t m, int64_t k,
+                          const float* global_sf_x_dev, uint8_t* codes_dev, uint8_t* scale_dev, float* gsf_out_dev,
+                          void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/*
+ * nvfp4_linear_swiglu: down_proj fed by its SwiGLU product, formed inside the
+ * quantizer as in nvfp4_quantize_swiglu: bit-identical to
+ * nvfp4_linear(nvfp4_swiglu(gate, up), m, k, ..., rotation_group 0).
+ * workspace: >= nvfp4_linear_swiglu_workspace_bytes(m, k, out_features) for a
+ * dynamic scale, nvfp4_linear_workspace_bytes for a static one.
+ */
+int nvfp4_linear_swiglu(const void* gate_dev, const void* up_dev, int64_t m, int64_t k,
+                        const uint8_t* packed_dev, const uint8_t* inv_scale_dev, const float* global_sf_w_dev,
+                        const void* bias_dev, int64_t out_features, const float* global_sf_x_dev, void* out_dev,
+                        void* workspace_dev, size_t workspace_bytes, void* stream);
 
 /*
  * nvfp4_dequantize: NVFP4 back to real values, the expansion the fused-dequant

@@ -32,9 +32,14 @@ SIGNATURES = {
     "nvfp4_linear_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "nvfp4_gemm_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "nvfp4_linear_segmented_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
+    "nvfp4_quantize_swiglu_workspace_bytes": (_sz, [_i64, _i64]),
+    "nvfp4_linear_swiglu_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "rotate_activation": (_int, [_vp, _int, _vp, _int, _i64, _i64, _int, _vp]),
     "nvfp4_quantize_weight": (_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_quantize_activation": (_int, [_vp, _i64, _i64, _vp, _int, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "nvfp4_swiglu": (_int, [_vp, _vp, _i64, _i64, _vp, _vp]),
+    "nvfp4_quantize_swiglu": (_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "nvfp4_linear_swiglu": (_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_dequantize": (_int, [_vp, _vp, _i64, _i64, _vp, _vp, _int, _vp]),
     "nvfp4_amax": (_int, [_vp, _i64, _i64, _int, _vp, _int, _vp, _sz, _vp]),
     "nvfp4_static_global_scale": (_int, [_vp, ctypes.c_float, _vp, _vp]),

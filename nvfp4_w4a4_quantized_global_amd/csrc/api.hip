@@ -54,6 +54,12 @@ int check_group(const char* fn, int g, int64_t k, bool allow_none) {
 
 float inv_sqrt(int g) { return g > 1 ? (float)(1.0 / sqrt((double)g)) : 1.0f; }
 
+// The kernels read and write rows in 16-byte pieces.
+int check_aligned(const char* fn, const char* what, const void* p) {
+  if ((uintptr_t)p % 16) return fail(NVFP4_ERR_ARG, "%s: %s must be 16-byte aligned", fn, what);
+  return NVFP4_OK;
+}
+
 struct LinearWorkspace {
   uint8_t* codes;
   uint8_t* scales;
@@ -88,24 +94,36 @@ LinearWorkspace carve(void* base, int64_t m, int64_t k, int64_t n, int64_t segme
 
 // Rows form `segments` consecutive blocks of m / segments rows; with a dynamic scale
 // each block gets its own global scale (gsf_out[segment]).
+// With `up` not NULL the input is the SwiGLU product of x (gate) and up.  A static
+// scale forms it inside the single quantize pass; a dynamic one forms it once in the
+// amax pass, which stores it in xbuf ([m][k] bf16) for the quantize pass to read.
 int quantize_impl(const char* fn, const void* x, int64_t m, int64_t k, const float* gsf_static, int group,
                   uint8_t* codes, uint8_t* scales, float* gsf_out, float* partials, hipStream_t s,
-                  int64_t segments = 1) {
+                  int64_t segments = 1, const void* up = nullptr, void* xbuf = nullptr) {
   int n_partials = 0;
   const float c = inv_sqrt(group);
   const int64_t seg_rows = m / segments;
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  const uint16_t* upp = static_cast<const uint16_t*>(up);
   if (gsf_static == nullptr) {
-    int rc = hip_status(nvfp4::launch_amax_partials(static_cast<const uint16_t*>(x), seg_rows, k, (int)segments,
-                                                    group, c, partials, &n_partials, s), fn);
+    uint16_t* xout = upp != nullptr ? static_cast<uint16_t*>(xbuf) : nullptr;
+    int rc = hip_status(nvfp4::launch_amax_partials(xp, upp, xout, seg_rows, k, (int)segments, group, c, partials,
+                                                    &n_partials, s), fn);
     if (rc) return rc;
+    if (xout != nullptr) {
+      xp = xout;
+      upp = nullptr;
+    }
   }
-  return hip_status(nvfp4::launch_quantize(static_cast<const uint16_t*>(x), m, k, group, c, gsf_static, partials,
-                                           n_partials, seg_rows, (int)segments, codes, scales, gsf_out, s), fn);
+  return hip_status(nvfp4::launch_quantize(xp, upp, m, k, group, c, gsf_static, partials, n_partials, seg_rows,
+                                           (int)segments, codes, scales, gsf_out, s), fn);
 }
 
+size_t product_bytes(int64_t m, int64_t k) { return align_up((size_t)m * (size_t)k * 2u); }
+
 int check_segments(const char* fn, int64_t segments, int64_t seg_rows) {
-  if (segments < 1 || segments > nvfp4::kMaxAmaxPartials)
-    return fail(NVFP4_ERR_ARG, "%s: segments must be in [1, %d], got %lld", fn, nvfp4::kMaxAmaxPartials,
+  if (segments < 1 || segments > nvfp4::kMaxSegments)
+    return fail(NVFP4_ERR_ARG, "%s: segments must be in [1, %d], got %lld", fn, nvfp4::kMaxSegments,
                 (long long)segments);
   if (seg_rows < 0 || (double)segments * (double)seg_rows >= (double)kMaxDim)
     return fail(NVFP4_ERR_SHAPE, "%s: segments * seg_rows must be in [0, 2^31), got %lld * %lld", fn,
@@ -117,7 +135,9 @@ int check_segments(const char* fn, int64_t segments, int64_t seg_rows) {
 int linear_impl(const char* fn, const void* x, int64_t segments, int64_t seg_rows, int64_t k, const uint8_t* packed,
                 const uint8_t* inv_scale, const float* global_sf_w, const void* bias, int64_t out_features,
                 const float* global_sf_x, int rotation_group, void* out, float* gsf_out, void* workspace,
-                size_t workspace_bytes, hipStream_t s) {
+                size_t workspace_bytes, hipStream_t s, const void* up = nullptr) {
+  // a dynamic scale over a SwiGLU product keeps the product after the linear workspace
+  const bool keep_product = up != nullptr && global_sf_x == nullptr;
   const int64_t m = segments * seg_rows;
   if (int rc = check_rows_k(fn, m, k, true)) return rc;
   if (int rc = check_group(fn, rotation_group, k, true)) return rc;
@@ -125,15 +145,18 @@ int linear_impl(const char* fn, const void* x, int64_t segments, int64_t seg_row
     return fail(NVFP4_ERR_SHAPE, "%s: out_features must be in [1, 2^31), got %lld", fn, (long long)out_features);
   if (m == 0) return NVFP4_OK;
   if (!x || !packed || !inv_scale || !global_sf_w || !out) return fail(NVFP4_ERR_ARG, "%s: NULL tensor argument", fn);
-  const size_t need = carve(nullptr, m, k, out_features, segments).bytes;
+  if (int rc = check_aligned(fn, "x", x)) return rc;
+  const size_t base = carve(nullptr, m, k, out_features, segments).bytes;
+  const size_t need = base + (keep_product ? product_bytes(m, k) : 0);
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % NVFP4_WORKSPACE_ALIGN))
     return fail(NVFP4_ERR_WORKSPACE, "%s: need a %d-byte aligned workspace of %zu bytes, got %zu", fn,
                 NVFP4_WORKSPACE_ALIGN, need, workspace_bytes);
   const LinearWorkspace ws = carve(workspace, m, k, out_features, segments);
   float* gsf = gsf_out != nullptr ? gsf_out : ws.gsf;   // the GEMM reads the scales where they were written
   const bool per_segment = global_sf_x == nullptr && segments > 1;
+  void* xbuf = keep_product ? static_cast<uint8_t*>(workspace) + base : nullptr;
   if (int rc = quantize_impl(fn, x, m, k, global_sf_x, rotation_group, ws.codes, ws.scales, gsf, ws.partials, s,
-                             per_segment ? segments : 1))
+                             per_segment ? segments : 1, up, xbuf))
     return rc;
   return hip_status(nvfp4::launch_gemm(ws.codes, ws.scales, m, k, packed, inv_scale, out_features, gsf, global_sf_w,
                                        per_segment ? seg_rows : 0, static_cast<const uint16_t*>(bias),
@@ -159,8 +182,18 @@ size_t nvfp4_linear_workspace_bytes(int64_t m, int64_t k, int64_t n) {
 }
 
 size_t nvfp4_linear_segmented_workspace_bytes(int64_t segments, int64_t seg_rows, int64_t k, int64_t n) {
-  if (segments < 1 || segments > nvfp4::kMaxAmaxPartials || seg_rows < 0 || k <= 0 || n <= 0) return 0;
+  if (segments < 1 || segments > nvfp4::kMaxSegments || seg_rows < 0 || k <= 0 || n <= 0) return 0;
   return carve(nullptr, segments * seg_rows, k, n, segments).bytes;
+}
+
+size_t nvfp4_quantize_swiglu_workspace_bytes(int64_t m, int64_t k) {
+  if (m < 0 || k <= 0) return 0;
+  return nvfp4_quantize_workspace_bytes() + product_bytes(m, k);
+}
+
+size_t nvfp4_linear_swiglu_workspace_bytes(int64_t m, int64_t k, int64_t n) {
+  if (m < 0 || k <= 0 || n <= 0) return 0;
+  return carve(nullptr, m, k, n).bytes + product_bytes(m, k);
 }
 
 size_t nvfp4_gemm_workspace_bytes(int64_t m, int64_t k, int64_t n) {
@@ -181,6 +214,8 @@ int rotate_activation(const void* x, int x_dtype, void* y, int y_dtype, int64_t 
     return fail(NVFP4_ERR_ARG, "%s: dtype must be NVFP4_DTYPE_BF16 or NVFP4_DTYPE_F32", fn);
   if (rows == 0) return NVFP4_OK;
   if (x == nullptr || y == nullptr) return fail(NVFP4_ERR_ARG, "%s: x and y must not be NULL", fn);
+  if (int rc = check_aligned(fn, "x", x)) return rc;
+  if (int rc = check_aligned(fn, "y", y)) return rc;
   if (x == y && x_dtype != y_dtype) return fail(NVFP4_ERR_ARG, "%s: in-place rotation needs equal dtypes", fn);
   return hip_status(nvfp4::launch_rotate(x, x_dtype == NVFP4_DTYPE_BF16, y, y_dtype == NVFP4_DTYPE_BF16, rows, k,
                                          group_size, inv_sqrt(group_size), static_cast<hipStream_t>(stream)),
@@ -193,6 +228,7 @@ int nvfp4_quantize_weight(const void* w, int64_t n, int64_t k, uint8_t* packed, 
   g_err[0] = 0;
   if (int rc = check_rows_k(fn, n, k, false)) return rc;
   if (!w || !packed || !inv_scale || !global_sf_w) return fail(NVFP4_ERR_ARG, "%s: NULL tensor argument", fn);
+  if (int rc = check_aligned(fn, "w", w)) return rc;
   if (!workspace || workspace_bytes < nvfp4_quantize_workspace_bytes() ||
       ((uintptr_t)workspace % NVFP4_WORKSPACE_ALIGN))
     return fail(NVFP4_ERR_WORKSPACE, "%s: need a %d-byte aligned workspace of %zu bytes, got %zu", fn,
@@ -210,6 +246,7 @@ int nvfp4_quantize_activation(const void* x, int64_t m, int64_t k, const float* 
   if (int rc = check_group(fn, rotation_group, k, true)) return rc;
   if (m == 0) return NVFP4_OK;
   if (!x || !codes || !scales) return fail(NVFP4_ERR_ARG, "%s: NULL tensor argument", fn);
+  if (int rc = check_aligned(fn, "x", x)) return rc;
   if (global_sf_x == nullptr &&
       (!workspace || workspace_bytes < nvfp4_quantize_workspace_bytes() ||
        ((uintptr_t)workspace % NVFP4_WORKSPACE_ALIGN)))
@@ -227,6 +264,8 @@ int nvfp4_amax(const void* x, int64_t rows, int64_t k, int rotation_group, float
   if (int rc = check_group(fn, rotation_group, k, true)) return rc;
   if (!amax) return fail(NVFP4_ERR_ARG, "%s: amax must not be NULL", fn);
   if (rows > 0 && !x) return fail(NVFP4_ERR_ARG, "%s: x must not be NULL", fn);
+  if (rows > 0)
+    if (int rc = check_aligned(fn, "x", x)) return rc;
   if (!workspace || workspace_bytes < nvfp4_quantize_workspace_bytes() ||
       ((uintptr_t)workspace % NVFP4_WORKSPACE_ALIGN))
     return fail(NVFP4_ERR_WORKSPACE, "%s: need a %d-byte aligned workspace of %zu bytes", fn, NVFP4_WORKSPACE_ALIGN,
@@ -235,11 +274,55 @@ int nvfp4_amax(const void* x, int64_t rows, int64_t k, int rotation_group, float
   float* partials = static_cast<float*>(workspace);
   int n_partials = 0;
   if (rows > 0) {
-    int rc = hip_status(nvfp4::launch_amax_partials(static_cast<const uint16_t*>(x), rows, k, 1, rotation_group,
+    int rc = hip_status(nvfp4::launch_amax_partials(static_cast<const uint16_t*>(x), nullptr, nullptr, rows, k, 1,
+                                                    rotation_group,
                                                     inv_sqrt(rotation_group), partials, &n_partials, s), fn);
     if (rc) return rc;
   }
   return hip_status(nvfp4::launch_amax_finalize(partials, n_partials, amax, accumulate != 0, s), fn);
+}
+
+int nvfp4_swiglu(const void* gate, const void* up, int64_t rows, int64_t k, void* x, void* stream) {
+  const char* fn = "nvfp4_swiglu";
+  g_err[0] = 0;
+  if (int rc = check_rows_k(fn, rows, k, true)) return rc;
+  if (rows == 0) return NVFP4_OK;
+  if (!gate || !up || !x) return fail(NVFP4_ERR_ARG, "%s: NULL tensor argument", fn);
+  if (((uintptr_t)gate | (uintptr_t)up | (uintptr_t)x) % 16)
+    return fail(NVFP4_ERR_ARG, "%s: tensors must be 16-byte aligned", fn);
+  return hip_status(nvfp4::launch_swiglu(static_cast<const uint16_t*>(gate), static_cast<const uint16_t*>(up),
+                                         static_cast<uint16_t*>(x), rows, k, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int nvfp4_quantize_swiglu(const void* gate, const void* up, int64_t m, int64_t k, const float* global_sf_x,
+                          uint8_t* codes, uint8_t* scales, float* gsf_out, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  const char* fn = "nvfp4_quantize_swiglu";
+  g_err[0] = 0;
+  if (int rc = check_rows_k(fn, m, k, true)) return rc;
+  if (m == 0) return NVFP4_OK;
+  if (!gate || !up || !codes || !scales) return fail(NVFP4_ERR_ARG, "%s: NULL tensor argument", fn);
+  if (((uintptr_t)gate | (uintptr_t)up) % 16) return fail(NVFP4_ERR_ARG, "%s: gate and up must be 16-byte aligned", fn);
+  const size_t need = nvfp4_quantize_swiglu_workspace_bytes(m, k);
+  if (global_sf_x == nullptr &&
+      (!workspace || workspace_bytes < need || ((uintptr_t)workspace % NVFP4_WORKSPACE_ALIGN)))
+    return fail(NVFP4_ERR_WORKSPACE, "%s: the dynamic scale needs a %d-byte aligned workspace of %zu bytes", fn,
+                NVFP4_WORKSPACE_ALIGN, need);
+  void* xbuf = global_sf_x == nullptr ? static_cast<uint8_t*>(workspace) + nvfp4_quantize_workspace_bytes() : nullptr;
+  return quantize_impl(fn, gate, m, k, global_sf_x, 0, codes, scales, gsf_out, static_cast<float*>(workspace),
+                       static_cast<hipStream_t>(stream), 1, up, xbuf);
+}
+
+int nvfp4_linear_swiglu(const void* gate, const void* up, int64_t m, int64_t k, const uint8_t* packed,
+                        const uint8_t* inv_scale, const float* global_sf_w, const void* bias, int64_t out_features,
+                        const float* global_sf_x, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "nvfp4_linear_swiglu";
+  g_err[0] = 0;
+  if (m > 0 && !up) return fail(NVFP4_ERR_ARG, "%s: NULL tensor argument", fn);
+  if (((uintptr_t)gate | (uintptr_t)up) % 16) return fail(NVFP4_ERR_ARG, "%s: gate and up must be 16-byte aligned", fn);
+  return linear_impl(fn, gate, 1, m, k, packed, inv_scale, global_sf_w, bias, out_features, global_sf_x, 0, out,
+                     nullptr, workspace, workspace_bytes, static_cast<hipStream_t>(stream), up);
 }
 
 int nvfp4_dequantize(const uint8_t* packed, const uint8_t* scales, int64_t rows, int64_t k, const float* global_sf,
@@ -278,6 +361,7 @@ int nvfp4_quantize_activation_segmented(const void* x, int64_t segments, int64_t
   if (int rc = check_group(fn, rotation_group, k, true)) return rc;
   if (m == 0) return NVFP4_OK;
   if (!x || !codes || !scales || !gsf_out) return fail(NVFP4_ERR_ARG, "%s: NULL tensor argument", fn);
+  if (int rc = check_aligned(fn, "x", x)) return rc;
   if (!workspace || workspace_bytes < nvfp4_quantize_workspace_bytes() ||
       ((uintptr_t)workspace % NVFP4_WORKSPACE_ALIGN))
     return fail(NVFP4_ERR_WORKSPACE, "%s: need a %d-byte aligned workspace of %zu bytes", fn, NVFP4_WORKSPACE_ALIGN,

@@ -44,6 +44,31 @@ __device__ __forceinline__ float e4m3_decode(uint32_t b) {
   return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
 }
 
+// SwiGLU product feeding down_proj: bf16(fp32(fp32(g / fp32(1 + exp(-g))) * u)).  exp is
+// evaluated in fp32 step by step: clamp to [-80, 80], t = n*ln2 + r by Cody-Waite
+// reduction (ln2 = 15-bit head + tail, so n*head is exact), e^r by a degree-6 Taylor
+// polynomial in Horner form, then the exact scaling by 2^n.  Each step is one IEEE
+// fp32 operation (explicit intrinsics: no contraction), which fixes the result bit for
+// bit; it is within 3 ulps of exp.
+__device__ __forceinline__ float exp_cw(float t) {
+  t = fminf(fmaxf(t, -80.0f), 80.0f);
+  const float n = __builtin_rintf(__fmul_rn(t, 0x1.715476p+0f));
+  const float r = __fsub_rn(__fsub_rn(t, __fmul_rn(n, 0x1.62e4p-1f)), __fmul_rn(n, 0x1.7f7d1cp-20f));
+  float p = 0x1.6c16c2p-10f;                       // 1/720
+  p = __fadd_rn(__fmul_rn(p, r), 0x1.111112p-7f);  // 1/120
+  p = __fadd_rn(__fmul_rn(p, r), 0x1.555556p-5f);  // 1/24
+  p = __fadd_rn(__fmul_rn(p, r), 0x1.555556p-3f);  // 1/6
+  p = __fadd_rn(__fmul_rn(p, r), 0.5f);
+  p = __fadd_rn(__fmul_rn(p, r), 1.0f);
+  p = __fadd_rn(__fmul_rn(p, r), 1.0f);
+  return __builtin_ldexpf(p, (int)n);
+}
+
+__device__ __forceinline__ float swiglu_bf16(float g, float u) {
+  const float d = __fadd_rn(1.0f, exp_cw(-g));
+  return bf16_to_f32(f32_to_bf16(__fmul_rn(__fdiv_rn(g, d), u)));
+}
+
 // E2M1 nibble -> fp32, exact: magnitudes 0, .5, 1, 1.5 for codes 0-3, then
 // 2^(e-1) * (1 + m/2) for codes 4-7 (e = code >> 1, m = code & 1); bit 3 is the sign.
 __device__ __forceinline__ float e2m1_decode(uint32_t c) {

@@ -8,20 +8,29 @@
 
 namespace nvfp4 {
 
-// Upper bound on the number of per-block partial maxima of the amax pass.
-constexpr int kMaxAmaxPartials = 1024;
+// Upper bound on the number of per-block partial maxima of the amax pass, and on the
+// number of segments (row blocks with their own scale) of one call.
+constexpr int kMaxAmaxPartials = 4096;
+constexpr int kMaxSegments = 1024;
 
 // Partial maxima of `segments` consecutive row blocks of seg_rows rows each (one
-// segment for a plain call): partials[seg * (*n_partials) + i].
-hipError_t launch_amax_partials(const uint16_t* x, int64_t seg_rows, int64_t k, int segments, int group,
-                                float inv_sqrt_g, float* partials, int* n_partials, hipStream_t s);
+// segment for a plain call): partials[seg * (*n_partials) + i].  With `up` not NULL the
+// input is the bf16 SwiGLU product of x (gate) and up, computed on the fly and, if
+// xout is not NULL, stored there.
+hipError_t launch_amax_partials(const uint16_t* x, const uint16_t* up, uint16_t* xout, int64_t seg_rows, int64_t k,
+                                int segments, int group, float inv_sqrt_g, float* partials, int* n_partials,
+                                hipStream_t s);
 
 // Quantizes rows x [rows][k]; with static_gsf NULL, segment s (rows [s*seg_rows,
 // (s+1)*seg_rows)) takes its global scale from its n_partials partial maxima and
 // gsf_out[s] receives it.
-hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t k, int group, float inv_sqrt_g,
-                           const float* static_gsf, const float* partials, int n_partials, int64_t seg_rows,
-                           int segments, uint8_t* codes, uint8_t* scales, float* gsf_out, hipStream_t s);
+hipError_t launch_quantize(const uint16_t* x, const uint16_t* up, int64_t rows, int64_t k, int group,
+                           float inv_sqrt_g, const float* static_gsf, const float* partials, int n_partials,
+                           int64_t seg_rows, int segments, uint8_t* codes, uint8_t* scales, float* gsf_out,
+                           hipStream_t s);
+
+// x [rows][k] = bf16 SwiGLU product of gate and up.
+hipError_t launch_swiglu(const uint16_t* gate, const uint16_t* up, uint16_t* x, int64_t rows, int64_t k, hipStream_t s);
 
 // NVFP4 [rows][k] (codes + scales in the library layout) -> bf16 or fp32 values
 // fp32(code * scale) / gsf.

@@ -20,7 +20,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kAmaxBlocks = 512;   // partial maxima of the amax pass (<= kMaxAmaxPartials)
-static_assert(kAmaxBlocks <= kMaxAmaxPartials, "partials buffer");
+static_assert(8 * kAmaxBlocks <= kMaxAmaxPartials, "partials buffer");
 
 struct Chunk16 {
   float v[16];
@@ -65,30 +65,64 @@ __device__ __forceinline__ float block_max(float x, float* lds) {
 // kAmaxUnroll chunks in flight.
 constexpr int kAmaxUnroll = 4;
 
+// Stores 16 values that are already bf16-exact as bf16.
+__device__ __forceinline__ void store16_bf16(uint16_t* __restrict__ p, const float (&v)[16]) {
+  uint32_t w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = (__float_as_uint(v[2 * i]) >> 16) | (__float_as_uint(v[2 * i + 1]) & 0xFFFF0000u);
+  uint4* d = reinterpret_cast<uint4*>(p);
+  d[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  d[1] = make_uint4(w[4], w[5], w[6], w[7]);
+}
+
+// Loads 16 input values at element offset off: x itself, or with kSwiglu the bf16
+// SwiGLU product of x (gate) and u (up).
+template <bool kSwiglu>
+__device__ __forceinline__ void load_input16(const uint16_t* __restrict__ x, const uint16_t* __restrict__ u,
+                                             int64_t off, float (&v)[16]) {
+  load16_bf16(x + off, v);
+  if (kSwiglu) {
+    float w[16];
+    load16_bf16(u + off, w);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = swiglu_bf16(v[i], w[i]);
+  }
+}
+
 // Segments (blockIdx.y) are consecutive row blocks of n_chunks chunks each, reduced
-// separately into partials[blockIdx.y * gridDim.x + blockIdx.x].
-template <bool kRotate>
-__global__ void __launch_bounds__(kThreads) amax_partial_kernel(const uint16_t* __restrict__ x, int64_t n_chunks,
+// separately into partials[blockIdx.y * gridDim.x + blockIdx.x].  With kSwiglu the
+// input is formed from gate (x) and up and, when xout is not NULL, also stored there,
+// so the quantize pass reads the product instead of forming it again.
+template <bool kRotate, bool kSwiglu>
+__global__ void __launch_bounds__(kThreads) amax_partial_kernel(const uint16_t* __restrict__ x,
+                                                                 const uint16_t* __restrict__ up,
+                                                                 uint16_t* __restrict__ xout, int64_t n_chunks,
                                                                  int group, float inv_sqrt_g,
                                                                  float* __restrict__ partials) {
   __shared__ float lds[kThreads / 64];
   x += (int64_t)blockIdx.y * n_chunks * 16;
+  if (kSwiglu) up += (int64_t)blockIdx.y * n_chunks * 16;
+  if (kSwiglu && xout != nullptr) xout += (int64_t)blockIdx.y * n_chunks * 16;
+  // memory-bound plain input: several chunks in flight per lane; the ALU-bound SwiGLU
+  // product: one, for more waves per SIMD
+  constexpr int kUnroll = kSwiglu ? 1 : kAmaxUnroll;
   float m = 0.0f;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t c0 = (int64_t)blockIdx.x * kThreads; c0 < n_chunks; c0 += stride * kAmaxUnroll) {
-    float v[kAmaxUnroll][16];
+  for (int64_t c0 = (int64_t)blockIdx.x * kThreads; c0 < n_chunks; c0 += stride * kUnroll) {
+    float v[kUnroll][16];
 #pragma unroll
-    for (int u = 0; u < kAmaxUnroll; ++u) {
+    for (int u = 0; u < kUnroll; ++u) {
       const int64_t c = c0 + u * stride + threadIdx.x;
       if (c < n_chunks) {
-        load16_bf16(x + c * 16, v[u]);
+        load_input16<kSwiglu>(x, up, c * 16, v[u]);
+        if (kSwiglu && xout != nullptr) store16_bf16(xout + c * 16, v[u]);
       } else {
 #pragma unroll
         for (int i = 0; i < 16; ++i) v[u][i] = 0.0f;
       }
     }
 #pragma unroll
-    for (int u = 0; u < kAmaxUnroll; ++u) {
+    for (int u = 0; u < kUnroll; ++u) {
       if (kRotate) rotate16_bf16(v[u], group, inv_sqrt_g);
 #pragma unroll
       for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[u][i]));
@@ -105,24 +139,37 @@ __global__ void __launch_bounds__(kThreads) amax_partial_kernel(const uint16_t* 
 // global scale once, then loop over groups of kQuantUnits x 32 units, loading a
 // group's units before computing them.
 constexpr int kQuantUnits = 2;
-constexpr int kQuantBlocks = 2048;   // grid cap: blocks loop over the units
+// Grid cap (blocks loop over the units): more blocks in flight pay off once the input
+// is several times larger than one pass of the cap; below that the per-block scale
+// prologue dominates.
+constexpr int kQuantBlocks = 2048;
+constexpr int kQuantBlocksLarge = 8192;
+constexpr int64_t kLargeUnits = (int64_t)1 << 19;
 
 // With a dynamic scale the rows form `segments` consecutive blocks of seg_rows rows,
 // each with its own global scale from its own n_partials partial maxima (one segment
 // for a plain call); gsf_out receives one scale per segment.
-template <bool kRotate>
+template <bool kRotate, bool kSwiglu>
 __global__ void __launch_bounds__(kThreads) quantize_kernel(
-    const uint16_t* __restrict__ x, int64_t m_rows, int64_t k, int group, float inv_sqrt_g,
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ up, int64_t m_rows, int64_t k, int group,
+    float inv_sqrt_g,
     const float* __restrict__ static_gsf, const float* __restrict__ partials, int n_partials, int64_t seg_rows,
     int segments, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gsf_out) {
-  __shared__ uint32_t seg_amax[kMaxAmaxPartials];   // segment maxima, then global scales (bits)
+  __shared__ uint32_t seg_amax[kMaxSegments];   // segment maxima, then global scales (bits)
+  __shared__ float lds[kThreads / 64];
   const int64_t kt_count = (k + kScaleTileK - 1) / kScaleTileK;
   const int64_t nb = k / kBlock;
   const int j = threadIdx.x & 7;
 
   const bool dynamic = static_gsf == nullptr;
   const float gsf_static = dynamic ? 0.0f : *static_gsf;
-  if (dynamic) {
+  if (dynamic && segments == 1) {
+    float a = 0.0f;
+    for (int i = threadIdx.x; i < n_partials; i += kThreads) a = fmaxf(a, partials[i]);
+    a = block_max(a, lds);
+    if (threadIdx.x == 0) seg_amax[0] = __float_as_uint(global_scale_from_amax(a));
+    __syncthreads();
+  } else if (dynamic) {
     // max of non-negative floats = max of their bit patterns
     for (int i = threadIdx.x; i < segments; i += kThreads) seg_amax[i] = 0u;
     __syncthreads();
@@ -153,7 +200,7 @@ __global__ void __launch_bounds__(kThreads) quantize_kernel(
       kt[u] = unit - row[u] * kt_count;
       const int64_t blk = kt[u] * 8 + j;
       if (row[u] < m_rows && blk < nb) {
-        load16_bf16(x + row[u] * k + blk * kBlock, v[u]);
+        load_input16<kSwiglu>(x, up, row[u] * k + blk * kBlock, v[u]);
       } else {
 #pragma unroll
         for (int i = 0; i < 16; ++i) v[u][i] = 0.0f;
@@ -310,35 +357,71 @@ int64_t grid_for(int64_t n_chunks, int64_t cap) {
 
 }  // namespace
 
-hipError_t launch_amax_partials(const uint16_t* x, int64_t seg_rows, int64_t k, int segments, int group,
-                                float inv_sqrt_g, float* partials, int* n_partials, hipStream_t s) {
+hipError_t launch_amax_partials(const uint16_t* x, const uint16_t* up, uint16_t* xout, int64_t seg_rows, int64_t k,
+                                int segments, int group, float inv_sqrt_g, float* partials, int* n_partials,
+                                hipStream_t s) {
   const int64_t n_chunks = seg_rows * k / kBlock;
-  int64_t cap = kAmaxBlocks / segments;
+  // the SwiGLU product costs ~45 VALU operations per value: more blocks in flight
+  int64_t cap = (up != nullptr ? 4 * kAmaxBlocks : kAmaxBlocks) / segments;
   if (cap < 1) cap = 1;
-  const int grid = (int)grid_for((n_chunks + kAmaxUnroll - 1) / kAmaxUnroll, cap);
+  const int unroll = up != nullptr ? 1 : kAmaxUnroll;
+  const int grid = (int)grid_for((n_chunks + unroll - 1) / unroll, cap);
   *n_partials = grid;
   const dim3 g3((uint32_t)grid, (uint32_t)segments);
-  if (group > 1)
-    hipLaunchKernelGGL(amax_partial_kernel<true>, g3, dim3(kThreads), 0, s, x, n_chunks, group, inv_sqrt_g, partials);
+  const bool rot = group > 1;
+  if (up != nullptr && rot)
+    hipLaunchKernelGGL((amax_partial_kernel<true, true>), g3, dim3(kThreads), 0, s, x, up, xout, n_chunks, group, inv_sqrt_g, partials);
+  else if (up != nullptr)
+    hipLaunchKernelGGL((amax_partial_kernel<false, true>), g3, dim3(kThreads), 0, s, x, up, xout, n_chunks, group, inv_sqrt_g, partials);
+  else if (rot)
+    hipLaunchKernelGGL((amax_partial_kernel<true, false>), g3, dim3(kThreads), 0, s, x, up, xout, n_chunks, group, inv_sqrt_g, partials);
   else
-    hipLaunchKernelGGL(amax_partial_kernel<false>, g3, dim3(kThreads), 0, s, x, n_chunks, group, inv_sqrt_g, partials);
+    hipLaunchKernelGGL((amax_partial_kernel<false, false>), g3, dim3(kThreads), 0, s, x, up, xout, n_chunks, group, inv_sqrt_g, partials);
   return hipGetLastError();
 }
 
-hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t k, int group, float inv_sqrt_g,
-                           const float* static_gsf, const float* partials, int n_partials, int64_t seg_rows,
-                           int segments, uint8_t* codes, uint8_t* scales, float* gsf_out, hipStream_t s) {
+hipError_t launch_quantize(const uint16_t* x, const uint16_t* up, int64_t rows, int64_t k, int group,
+                           float inv_sqrt_g, const float* static_gsf, const float* partials, int n_partials,
+                           int64_t seg_rows, int segments, uint8_t* codes, uint8_t* scales, float* gsf_out,
+                           hipStream_t s) {
   const int64_t kt_count = (k + kScaleTileK - 1) / kScaleTileK;
   const int64_t units = rows * kt_count;
   const int64_t per_block = (int64_t)kQuantUnits * (kThreads / 8);
   int64_t grid = (units + per_block - 1) / per_block;
-  if (grid > kQuantBlocks) grid = kQuantBlocks;
-  if (group > 1)
-    hipLaunchKernelGGL(quantize_kernel<true>, dim3((uint32_t)grid), dim3(kThreads), 0, s, x, rows, k, group, inv_sqrt_g,
+  const int64_t cap = units > kLargeUnits ? kQuantBlocksLarge : kQuantBlocks;
+  if (grid > cap) grid = cap;
+  const dim3 g1((uint32_t)grid);
+  const bool rot = group > 1;
+  if (up != nullptr && rot)
+    hipLaunchKernelGGL((quantize_kernel<true, true>), g1, dim3(kThreads), 0, s, x, up, rows, k, group, inv_sqrt_g,
+                       static_gsf, partials, n_partials, seg_rows, segments, codes, scales, gsf_out);
+  else if (up != nullptr)
+    hipLaunchKernelGGL((quantize_kernel<false, true>), g1, dim3(kThreads), 0, s, x, up, rows, k, group, inv_sqrt_g,
+                       static_gsf, partials, n_partials, seg_rows, segments, codes, scales, gsf_out);
+  else if (rot)
+    hipLaunchKernelGGL((quantize_kernel<true, false>), g1, dim3(kThreads), 0, s, x, up, rows, k, group, inv_sqrt_g,
                        static_gsf, partials, n_partials, seg_rows, segments, codes, scales, gsf_out);
   else
-    hipLaunchKernelGGL(quantize_kernel<false>, dim3((uint32_t)grid), dim3(kThreads), 0, s, x, rows, k, group, inv_sqrt_g,
+    hipLaunchKernelGGL((quantize_kernel<false, false>), g1, dim3(kThreads), 0, s, x, up, rows, k, group, inv_sqrt_g,
                        static_gsf, partials, n_partials, seg_rows, segments, codes, scales, gsf_out);
+  return hipGetLastError();
+}
+
+// x = bf16 SwiGLU product of gate and up, one 16-value chunk per lane.
+__global__ void __launch_bounds__(kThreads) swiglu_kernel(const uint16_t* __restrict__ gate,
+                                                           const uint16_t* __restrict__ up, uint16_t* __restrict__ x,
+                                                           int64_t n_chunks) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < n_chunks; c += stride) {
+    float v[16];
+    load_input16<true>(gate, up, c * 16, v);
+    store16_bf16(x + c * 16, v);
+  }
+}
+
+hipError_t launch_swiglu(const uint16_t* gate, const uint16_t* up, uint16_t* x, int64_t rows, int64_t k, hipStream_t s) {
+  const int64_t n_chunks = rows * k / kBlock;
+  hipLaunchKernelGGL(swiglu_kernel, dim3((uint32_t)grid_for(n_chunks, 8192)), dim3(kThreads), 0, s, gate, up, x, n_chunks);
   return hipGetLastError();
 }
 

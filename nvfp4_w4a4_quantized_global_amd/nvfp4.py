@@ -226,6 +226,72 @@ def amax(x: torch.Tensor, rotation_group: int = 0, out: torch.Tensor | None = No
     return out
 
 
+def _gate_up(gate: torch.Tensor, up: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
+    if gate.shape != up.shape:
+        raise ValueError(f"gate and up must have the same shape, got {list(gate.shape)} and {list(up.shape)}")
+    k = gate.shape[-1]
+    g2, u2 = gate.reshape(-1, k), up.reshape(-1, k)
+    g2 = g2 if g2.is_contiguous() else g2.contiguous()
+    u2 = u2 if u2.is_contiguous() else u2.contiguous()
+    _require_cuda("gate", g2, torch.bfloat16, 2)
+    _require_cuda("up", u2, torch.bfloat16, 2)
+    return g2, u2
+
+
+def swiglu(gate: torch.Tensor, up: torch.Tensor) -> torch.Tensor:
+    """bf16 SwiGLU product silu(gate) * up (the input of down_proj)."""
+    g2, u2 = _gate_up(gate, up)
+    x = torch.empty(g2.shape, dtype=torch.bfloat16, device=gate.device)
+    check(lib().nvfp4_swiglu(_ptr(g2), _ptr(u2), g2.shape[0], g2.shape[1], _ptr(x), _stream(gate.device)))
+    return x.reshape(gate.shape)
+
+
+def quantize_swiglu(gate: torch.Tensor, up: torch.Tensor, global_sf_x=None
+                    ) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """quantize_activation(swiglu(gate, up)) without writing the product."""
+    g2, u2 = _gate_up(gate, up)
+    m, k = g2.shape
+    codes = torch.empty((m, k // 2), dtype=torch.uint8, device=gate.device)
+    scales = torch.empty((max(scale_bytes(m, k), 1),), dtype=torch.uint8, device=gate.device)
+    gsf = torch.empty((), dtype=torch.float32, device=gate.device)
+    g = None if global_sf_x is None else _scalar_f32(global_sf_x, gate.device)
+    ws = torch.empty((int(lib().nvfp4_quantize_swiglu_workspace_bytes(m, k)),), dtype=torch.uint8, device=gate.device)
+    check(lib().nvfp4_quantize_swiglu(_ptr(g2), _ptr(u2), m, k, _ptr(g), _ptr(codes), _ptr(scales), _ptr(gsf),
+                                      _ptr(ws), ws.numel(), _stream(gate.device)))
+    return codes, scales[: scale_bytes(m, k)], gsf
+
+
+def nvfp4_linear_swiglu(gate: torch.Tensor, up: torch.Tensor, packed: torch.Tensor, inv_scale: torch.Tensor,
+                        global_sf_w: torch.Tensor, bias: torch.Tensor | None, out_features: int, global_sf_x=None,
+                        workspace: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """down_proj on silu(gate) * up, the product never written (same result as
+    nvfp4_linear(swiglu(gate, up), ...))."""
+    g2, u2 = _gate_up(gate, up)
+    m, k = g2.shape
+    _require_cuda("packed", packed, torch.uint8, 2)
+    if packed.shape[0] != out_features or packed.shape[1] * 2 != k:
+        raise ValueError(f"packed NVFP4 weight must be uint8 [{out_features}, {k // 2}], got "
+                         f"{packed.dtype} {list(packed.shape)}")
+    _require_cuda("inv_scale", inv_scale, torch.uint8)
+    if inv_scale.numel() < scale_bytes(out_features, k):
+        raise ValueError("inv_scale is smaller than nvfp4_scale_bytes(out_features, K)")
+    gw = _scalar_f32(global_sf_w, gate.device)
+    gx = None if global_sf_x is None else _scalar_f32(global_sf_x, gate.device)
+    if bias is not None:
+        _require_cuda("bias", bias, torch.bfloat16)
+        if bias.numel() != out_features:
+            raise ValueError(f"bias must have {out_features} elements, got {bias.numel()}")
+    if workspace is None:
+        need = int(lib().nvfp4_linear_swiglu_workspace_bytes(m, k, out_features))
+        workspace = torch.empty((need,), dtype=torch.uint8, device=gate.device)
+    if out is None:
+        out = torch.empty((m, out_features), dtype=torch.bfloat16, device=gate.device)
+    check(lib().nvfp4_linear_swiglu(_ptr(g2), _ptr(u2), m, k, _ptr(packed), _ptr(inv_scale), _ptr(gw), _ptr(bias),
+                                    out_features, _ptr(gx), _ptr(out), _ptr(workspace), workspace.numel(),
+                                    _stream(gate.device)))
+    return out.reshape(*gate.shape[:-1], out_features)
+
+
 def dequantize(packed: torch.Tensor, scales: torch.Tensor, global_sf, dtype: torch.dtype = torch.bfloat16
                ) -> torch.Tensor:
     """NVFP4 [rows, K/2] + scales back to ``dtype`` values fp32(code * scale) / global_sf."""

@@ -37,7 +37,7 @@ import torch
 
 __all__ = [
     "Linear", "draw", "tiny_linear", "qwen3_attention", "qwen3_mlp", "vit_decoder_tiles",
-    "small_m_sweep", "small_m_weight", "small_m_input", "QWEN3_PROJECTIONS", "VIT_LINEARS", "headline_gate",
+    "small_m_sweep", "small_m_weight", "small_m_input", "down_proj_gate_up", "QWEN3_PROJECTIONS", "VIT_LINEARS", "headline_gate",
 ]
 
 # (name, out_features N, in_features K) of one Qwen3-32B-shaped decoder layer.
@@ -73,7 +73,9 @@ def draw(kind: str, shape: tuple[int, ...], seed: int, stream: int, scale: float
     kind: ``normal`` (N(0, scale^2)), ``t3`` (Student-t, 3 d.o.f., times scale),
     ``normal_outliers`` (N(0,1), 1% of entries multiplied by 20: the mask is
     drawn after the values, U[0,1) < 0.01), ``swiglu`` (silu(g) * u with g, u
-    independent N(0,1), computed in float32 before rounding).
+    independent N(0,1), computed in float32 before rounding: the heavy-tailed
+    data of a down_proj input given as a tensor; the library's own SwiGLU product,
+    formed from bf16 gate/up halves, is checked against the oracle instead).
     """
     rng = _rng(seed, stream)
     if kind == "normal":
@@ -153,6 +155,12 @@ def qwen3_mlp(seed: int = 2, m: int = 4096, which: tuple[str, ...] = ("gate", "u
         w = draw("normal", (n, k), seed, 10 + i, 0.02)
         out.append(Linear(name, xd, w))
     return out
+
+
+def down_proj_gate_up(seed: int = 2, m: int = 4096, k: int = 25600):
+    """The two bf16 halves feeding down_proj when its SwiGLU product is formed inside
+    the quantizer: gate and up activations, each N(0,1) bf16 [m, k]."""
+    return draw("normal", (m, k), seed, 3), draw("normal", (m, k), seed, 4)
 
 
 def headline_gate(seed: int = 2, m: int = 4096) -> Linear:
