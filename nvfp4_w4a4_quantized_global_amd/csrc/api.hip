@@ -152,6 +152,17 @@ int linear_impl(const char* fn, const void* x, int64_t segments, int64_t seg_row
     return fail(NVFP4_ERR_WORKSPACE, "%s: need a %d-byte aligned workspace of %zu bytes, got %zu", fn,
                 NVFP4_WORKSPACE_ALIGN, need, workspace_bytes);
   const LinearWorkspace ws = carve(workspace, m, k, out_features, segments);
+  if (global_sf_x != nullptr && rotation_group == 0 && up == nullptr && segments == 1 && gsf_out == nullptr &&
+      nvfp4::linear_skinny_fused_supported(m, k, out_features, x, packed, inv_scale, nvfp4::compute_units()) &&
+      ws.gemm_bytes >= nvfp4::gemm_workspace_bytes(m, k, out_features)) {
+    // static scale, few rows: quantized inside the weight-streaming GEMM, one launch
+    return hip_status(nvfp4::launch_linear_skinny_fused(static_cast<const uint16_t*>(x), m, k, packed, inv_scale,
+                                                        out_features, global_sf_x, global_sf_w,
+                                                        static_cast<const uint16_t*>(bias),
+                                                        static_cast<uint16_t*>(out), ws.gemm, ws.gemm_bytes,
+                                                        nvfp4::compute_units(), s),
+                      fn);
+  }
   float* gsf = gsf_out != nullptr ? gsf_out : ws.gsf;   // the GEMM reads the scales where they were written
   const bool per_segment = global_sf_x == nullptr && segments > 1;
   void* xbuf = keep_product ? static_cast<uint8_t*>(workspace) + base : nullptr;

@@ -35,8 +35,14 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 constexpr int kCols = 64;            // output columns per block (4 MFMA tiles of 16)
 constexpr int kWaves = 4;
 
-template <int MT>   // M tiles of 16 rows
+// kFusedA (MT == 1): A arrives as bf16 values (a_bf16, [m][k], m <= 16) with a static
+// global scale (*gsf_a).  The block first quantizes its K range of A into LDS, each
+// 16-block once and exactly as the quantize kernel would, and the waves then read A's
+// codes and scales from LDS instead of global memory.
+constexpr int kFusedMaxSt = 16;   // super tiles of A one block can stage
+template <int MT, bool kFusedA>   // M tiles of 16 rows
 __global__ void __launch_bounds__(256) gemm_skinny_kernel(
+    const uint16_t* __restrict__ a_bf16,
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m, int64_t k,
     const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, int64_t n,
     const float* __restrict__ gsf_a, const float* __restrict__ gsf_b, int64_t a_seg_rows,
@@ -70,8 +76,10 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
     const int64_t r = min((int64_t)(16 * i + l16), m - 1);
-    arow[i] = a_codes + r * half_k;
-    asrow[i] = a_scales + r * 8 + 4 * (g & 1);
+    if (!kFusedA) {
+      arow[i] = a_codes + r * half_k;
+      asrow[i] = a_scales + r * 8 + 4 * (g & 1);
+    }
   }
 
   float4_t acc[MT][4];
@@ -91,7 +99,7 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(
     uint4 ac[MT][2];
     uint32_t as[MT];
   };
-  auto fetch = [&](int64_t st, Tile& T) {
+  auto fetch_b = [&](int64_t st, Tile& T) {
     const int64_t off = st * 128 + 32 * g;           // code byte offset of this lane's 32 bytes
     const int64_t kt = 2 * st + (g >> 1);             // its scale tile
     const bool c0 = off < half_k, c1 = off + 16 < half_k, sv = kt < kt_all;   // partial last super tile
@@ -101,11 +109,25 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(
       T.bc[j][1] = c1 ? *reinterpret_cast<const uint4*>(brow[j] + off + 16) : make_uint4(0, 0, 0, 0);
       T.bs[j] = sv ? *reinterpret_cast<const uint32_t*>(bsrow[j] + kt * n * 8) : 0u;
     }
+  };
+  auto fetch_a = [&](int64_t st, Tile& T) {
+    const int64_t off = st * 128 + 32 * g;
+    const int64_t kt = 2 * st + (g >> 1);
+    const bool c0 = off < half_k, c1 = off + 16 < half_k, sv = kt < kt_all;
+    (void)c0; (void)c1; (void)sv;
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
-      T.ac[i][0] = c0 ? *reinterpret_cast<const uint4*>(arow[i] + off) : make_uint4(0, 0, 0, 0);
-      T.ac[i][1] = c1 ? *reinterpret_cast<const uint4*>(arow[i] + off + 16) : make_uint4(0, 0, 0, 0);
-      T.as[i] = sv ? *reinterpret_cast<const uint32_t*>(asrow[i] + kt * m * 8) : 0u;
+      if (kFusedA) {
+        // staged rows: code bytes [128 ls + 32 g, +32) and scale bytes [16 ls + 4 g, +4)
+        const int ls = (int)(st - st_begin);
+        T.ac[i][0] = *reinterpret_cast<const uint4*>(arow[i] + ls * 128 + 32 * g);
+        T.ac[i][1] = *reinterpret_cast<const uint4*>(arow[i] + ls * 128 + 32 * g + 16);
+        T.as[i] = *reinterpret_cast<const uint32_t*>(asrow[i] + ls * 16 + 4 * g);
+      } else {
+        T.ac[i][0] = c0 ? *reinterpret_cast<const uint4*>(arow[i] + off) : make_uint4(0, 0, 0, 0);
+        T.ac[i][1] = c1 ? *reinterpret_cast<const uint4*>(arow[i] + off + 16) : make_uint4(0, 0, 0, 0);
+        T.as[i] = sv ? *reinterpret_cast<const uint32_t*>(asrow[i] + kt * m * 8) : 0u;
+      }
     }
   };
   auto multiply = [&](const Tile& T) {
@@ -122,10 +144,38 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(
       }
     }
   };
+  auto fetch = [&](int64_t st, Tile& T) {
+    fetch_b(st, T);
+    fetch_a(st, T);
+  };
   int64_t st = st_begin + wave;
+  Tile cur;
+  if (st < st_end) fetch_b(st, cur);   // the first weight loads are in flight while A is staged
+  if constexpr (kFusedA) {  // quantize this block's K range of A into LDS
+    __shared__ __attribute__((aligned(16))) uint8_t a_codes_lds[16][kFusedMaxSt * 128];
+    __shared__ __attribute__((aligned(16))) uint8_t a_scales_lds[16][kFusedMaxSt * 16];
+    const float gsf_q = *gsf_a;
+    const int nblk = (int)(st_end - st_begin) * 16;        // 16-blocks of this K range per row
+    for (int q = threadIdx.x; q < m * nblk; q += 256) {
+      const int r = q / nblk, b = q - r * nblk;
+      const int64_t e0 = (st_begin * 16 + b) * (int64_t)kBlock;
+      float v[16];
+      if (e0 < k) {
+        load16_bf16(a_bf16 + r * k + e0, v);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = 0.0f;
+      }
+      uint32_t w0, w1;
+      a_scales_lds[r][b] = (uint8_t)quantize_block16(v, gsf_q, e0 < k, w0, w1);
+      *reinterpret_cast<uint2*>(&a_codes_lds[r][b * 8]) = make_uint2(w0, w1);
+    }
+    __syncthreads();
+    arow[0] = &a_codes_lds[min((int64_t)l16, m - 1)][0];
+    asrow[0] = &a_scales_lds[min((int64_t)l16, m - 1)][0];
+  }
   if (st < st_end) {
-    Tile cur;
-    fetch(st, cur);
+    fetch_a(st, cur);
     for (; st < st_end; st += kWaves) {
       Tile nxt;
       if (st + kWaves < st_end) fetch(st + kWaves, nxt);
@@ -208,17 +258,48 @@ int skinny_splits(int64_t k, int64_t n, int cus) {
   return (int)(sp < 1 ? 1 : sp);
 }
 
-template <int MT>
+template <int MT, bool kFusedA = false>
 hipError_t launch_mt(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, int64_t k, const uint8_t* b_codes,
                      const uint8_t* b_scales, int64_t n, const float* gsf_a, const float* gsf_b, const uint16_t* bias,
-                     int64_t a_seg_rows, uint16_t* out, int splits, float* partial, hipStream_t s) {
+                     int64_t a_seg_rows, uint16_t* out, int splits, float* partial, hipStream_t s,
+                     const uint16_t* a_bf16 = nullptr) {
   const int64_t groups = (n + kCols - 1) / kCols;
-  hipLaunchKernelGGL(gemm_skinny_kernel<MT>, dim3((uint32_t)(groups * splits)), dim3(256), 0, s, a_codes, a_scales,
-                     m, k, b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, splits, partial);
+  hipLaunchKernelGGL((gemm_skinny_kernel<MT, kFusedA>), dim3((uint32_t)(groups * splits)), dim3(256), 0, s, a_bf16,
+                     a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, splits,
+                     partial);
   return hipGetLastError();
 }
 
 }  // namespace
+
+bool linear_skinny_fused_supported(int64_t m, int64_t k, int64_t n, const void* x, const void* b_codes,
+                                   const void* b_scales, int cus) {
+  const int64_t st_all = ((k + BK - 1) / BK + 1) / 2;
+  const int sp = skinny_splits(k, n, cus);
+  const int64_t range = (st_all + sp - 1) / sp;     // super tiles a block stages
+  // staging costs about one 16-block per thread and row on the critical path: worth it
+  // while it stays within two per thread (measured: one row gains a launch, 16 rows lose)
+  return m >= 1 && m <= 16 && k % 32 == 0 && (((uintptr_t)x | (uintptr_t)b_codes) & 15) == 0 &&
+         ((uintptr_t)b_scales & 3) == 0 && range <= kFusedMaxSt && m * range * 16 <= 2 * 256;
+}
+
+hipError_t launch_linear_skinny_fused(const uint16_t* x, int64_t m, int64_t k, const uint8_t* b_codes,
+                                      const uint8_t* b_scales, int64_t n, const float* gsf_x, const float* gsf_w,
+                                      const uint16_t* bias, uint16_t* out, void* workspace, size_t workspace_bytes,
+                                      int cus, hipStream_t s) {
+  // the K range each block stages must fit its LDS: without the workspace for the
+  // planned split the caller takes the two-pass path
+  const int splits = skinny_splits(k, n, cus);
+  const size_t need = splits > 1 ? (size_t)splits * (size_t)m * (size_t)n * sizeof(float) : 0;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return hipErrorInvalidValue;
+  float* partial = splits > 1 ? static_cast<float*>(workspace) : nullptr;
+  hipError_t e = launch_mt<1, true>(nullptr, nullptr, m, k, b_codes, b_scales, n, gsf_x, gsf_w, bias, 0, out, splits,
+                                    partial, s, x);
+  if (e != hipSuccess || splits == 1) return e;
+  hipLaunchKernelGGL(gemm_skinny_reduce, dim3((uint32_t)((m * n + 255) / 256)), dim3(256), 0, s, partial, splits, m,
+                     n, gsf_x, gsf_w, (int64_t)0, bias, out);
+  return hipGetLastError();
+}
 
 bool gemm_skinny_supported(int64_t m, int64_t k, const void* a_codes, const void* a_scales, const void* b_codes,
                            const void* b_scales) {

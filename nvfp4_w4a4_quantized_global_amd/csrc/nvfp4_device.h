@@ -44,6 +44,18 @@ __device__ __forceinline__ float e4m3_decode(uint32_t b) {
   return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
 }
 
+// 16 consecutive bf16 values (32 bytes, 16-byte aligned) -> fp32.
+__device__ __forceinline__ void load16_bf16(const uint16_t* __restrict__ p, float (&v)[16]) {
+  const uint4 a = reinterpret_cast<const uint4*>(p)[0];
+  const uint4 b = reinterpret_cast<const uint4*>(p)[1];
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
 // SwiGLU product feeding down_proj: bf16(fp32(fp32(g / fp32(1 + exp(-g))) * u)).  exp is
 // evaluated in fp32 step by step: clamp to [-80, 80], t = n*ln2 + r by Cody-Waite
 // reduction (ln2 = 15-bit head + tail, so n*head is exact), e^r by a degree-6 Taylor
@@ -111,6 +123,27 @@ __device__ __forceinline__ uint32_t e2m1_encode8(const float* v) {
 __device__ __forceinline__ uint32_t block_scale_byte(float gsf, float bmax) {
   const float sf = __fdiv_rn(__fmul_rn(gsf, bmax), 6.0f);
   return e4m3_encode(sf);
+}
+
+// One 16-block under global scale gsf: its E4M3 scale byte and its 16 codes (two
+// words, value i in bits 4(i%8).. of word i/8).  All codes are 0 when the scale is 0.
+__device__ __forceinline__ uint32_t quantize_block16(const float (&v)[16], float gsf, bool valid, uint32_t& w0,
+                                                     uint32_t& w1) {
+  float bmax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) bmax = fmaxf(bmax, fabsf(v[i]));
+  const uint32_t s8 = valid ? block_scale_byte(gsf, bmax) : 0u;
+  w0 = 0;
+  w1 = 0;
+  if (s8 != 0) {
+    const float r = __fdiv_rn(gsf, e4m3_decode(s8));
+    float p[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[i] = __fmul_rn(v[i], r);
+    w0 = e2m1_encode8(p);
+    w1 = e2m1_encode8(p + 8);
+  }
+  return s8;
 }
 
 __device__ __forceinline__ float global_scale_from_amax(float amax) {

@@ -82,6 +82,17 @@ hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales, i
                               const float* gsf_b, int64_t a_seg_rows, const uint16_t* bias, uint16_t* out,
                               void* workspace, size_t workspace_bytes, int cus, hipStream_t s);
 
+// The whole linear for up to 16 activation rows with a static scale, in the
+// weight-streaming kernel: each block quantizes its K range of the bf16 rows x [m][k]
+// into LDS (same codes and scales as launch_quantize) instead of a separate pass.
+// Needs the workspace of gemm_skinny_workspace_bytes (hipErrorInvalidValue without).
+bool linear_skinny_fused_supported(int64_t m, int64_t k, int64_t n, const void* x, const void* b_codes,
+                                   const void* b_scales, int cus);
+hipError_t launch_linear_skinny_fused(const uint16_t* x, int64_t m, int64_t k, const uint8_t* b_codes,
+                                      const uint8_t* b_scales, int64_t n, const float* gsf_x, const float* gsf_w,
+                                      const uint16_t* bias, uint16_t* out, void* workspace, size_t workspace_bytes,
+                                      int cus, hipStream_t s);
+
 // Workspace the GEMM dispatcher can use for an [m, k] x [n, k] product (0 if none).
 size_t gemm_workspace_bytes(int64_t m, int64_t k, int64_t n);
 

@@ -26,17 +26,6 @@ struct Chunk16 {
   float v[16];
 };
 
-__device__ __forceinline__ void load16_bf16(const uint16_t* __restrict__ p, float (&v)[16]) {
-  const uint4 a = reinterpret_cast<const uint4*>(p)[0];
-  const uint4 b = reinterpret_cast<const uint4*>(p)[1];
-  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    v[2 * i] = __uint_as_float(w[i] << 16);
-    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-  }
-}
-
 __device__ __forceinline__ void load16_f32(const float* __restrict__ p, float (&v)[16]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -214,19 +203,8 @@ __global__ void __launch_bounds__(kThreads) quantize_kernel(
       const bool in_row = row[u] < m_rows;
       const bool valid = in_row && blk < nb;
       const float gsf = dynamic ? __uint_as_float(seg_amax[in_row ? row[u] / seg_rows : 0]) : gsf_static;
-      float bmax = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) bmax = fmaxf(bmax, fabsf(v[u][i]));
-      const uint32_t s8 = valid ? block_scale_byte(gsf, bmax) : 0u;
-      uint32_t w0 = 0, w1 = 0;
-      if (s8 != 0) {
-        const float r = __fdiv_rn(gsf, e4m3_decode(s8));
-        float p[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) p[i] = __fmul_rn(v[u][i], r);
-        w0 = e2m1_encode8(p);
-        w1 = e2m1_encode8(p + 8);
-      }
+      uint32_t w0, w1;
+      const uint32_t s8 = quantize_block16(v[u], gsf, valid, w0, w1);
       if (valid) *reinterpret_cast<uint2*>(codes + row[u] * (k / 2) + blk * 8) = make_uint2(w0, w1);
       // gather the unit's 8 scale bytes into lane j == 0 and write them as one 8-byte word
       uint32_t lo = j < 4 ? s8 << (8 * j) : 0u;

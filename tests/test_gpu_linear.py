@@ -291,3 +291,28 @@ def test_calibration_then_static_forward():
     tile = x[:rows]
     out = layer(tile)
     check_against_oracle(lin, lin.x[:rows], out, layer.packed, layer.inv_scale, layer.global_sf_w, gx, g)
+
+
+@pytest.mark.parametrize("m", [1, 5, 16])
+@pytest.mark.parametrize("n,k", [(1024, 5120), (300, 4128), (5120, 1024)])
+def test_static_decode_fused_quantize(m, n, k):
+    """Static scale, up to 16 rows: nvfp4_linear quantizes inside the weight-streaming GEMM;
+    bit-identical to quantizing first and running nvfp4_gemm, and within tolerance of the
+    oracle.  The scale saturates some blocks (static range below the true amax)."""
+    x = workloads.draw("t3", (m, k), m + k, 0, 2.0)
+    w = workloads.draw("normal", (n, k), 31, n, 0.02)
+    bias = workloads.draw("normal", (n,), 32, n, 0.01)
+    packed, inv_scale, gsf_w = nv().quantize_weight(w.to(DEV))
+    xf = x.float().numpy()
+    gx = o.global_sf(np.float32(0.5) * o.amax(xf))
+    gxt = torch.tensor(float(gx), dtype=torch.float32, device=DEV)
+    fused = nv().nvfp4_linear(x.to(DEV), packed, inv_scale, gsf_w, bias.to(DEV), n, gxt)
+    codes, scales, _ = nv().quantize_activation(x.to(DEV), gxt)
+    two = nv().nvfp4_gemm(codes, scales, packed, inv_scale, gxt, gsf_w, bias.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(fused, two)
+    pw, sw, gw = o.quantize_weight(w.float().numpy())
+    r = o.nvfp4_linear_inference(xf, pw, sw, gw, bias.float().numpy(), gx)
+    assert np.array_equal(codes.cpu().numpy(), r["codes"])
+    bound = accumulation_bound(o.dequantize(r["codes"], r["scales"]), o.dequantize(pw, sw), r["alpha"])
+    assert_gemm_close(fused.float().cpu().numpy(), r["out"], bound)
