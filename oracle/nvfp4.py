@@ -52,7 +52,8 @@ rounded to bf16 again.
 
 Parity unpinned (fixed only by these readings, not by anything the pages
 print): the nibble order, the sign of zero codes, the scale/code expression
-order, the FWHT stage order, and which Hadamard matrix.
+order, the FWHT stage order, which Hadamard matrix, and the exp algorithm of the
+SwiGLU product (pinned to float64 within its error, not to a unique result).
 
 All floating point that decides a code or a scale byte is IEEE float32 (the
 precision the GPU kernels use); the matmul accumulates in float64.
