@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=30)
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
     p.add_argument("--cpu-rows", type=int, default=M, help="rows of the CPU oracle sample")
+    p.add_argument("--cpu-repeats", type=int, default=4,
+                   help="times the oracle runs the sample (the rate is the total work over the total time)")
     p.add_argument("--part", choices=("step", "gemm", "quantize", "copy"),
                    help="run only this part (warmup + steps launches, no JSON line): for counter runs")
     p.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
@@ -150,9 +152,10 @@ def time_on_stream(fn, iters: int, stream) -> float:
     return start.elapsed_time(end) / iters
 
 
-def cpu_baseline(x_cpu, w_cpu, rows: int) -> dict:
+def cpu_baseline(x_cpu, w_cpu, rows: int, repeats: int = 1) -> dict:
     """The oracle, untuned, on `rows` rows of the same linear (weights pre-quantized,
-    untimed): amax, quantize, dequantize, float64 GEMM over all N outputs, epilogue."""
+    untimed), `repeats` times: amax, quantize, dequantize, float64 GEMM over all N
+    outputs, epilogue."""
     import numpy as np
     import oracle as o
     try:
@@ -164,13 +167,14 @@ def cpu_baseline(x_cpu, w_cpu, rows: int) -> dict:
     pw, sw, gw = o.quantize_weight(wf)
     xs = x_cpu[:rows].float().numpy()
     t0 = time.perf_counter()
-    o.nvfp4_linear_inference(xs, pw, sw, gw, None)
+    for _ in range(repeats):
+        o.nvfp4_linear_inference(xs, pw, sw, gw, None)
     dt = time.perf_counter() - t0
-    flops = 2.0 * rows * N * K
+    flops = 2.0 * rows * N * K * repeats
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas_threads),
             "kind": "oracle",
-            "sample": f"{rows} of {M} rows of the [{M},{K}]x[{N},{K}] linear (amax, quantize, dequantize, "
-                      f"float64 GEMM, epilogue), weights pre-quantized; {dt:.2f} s",
+            "sample": f"{repeats} x {rows} of {M} rows of the [{M},{K}]x[{N},{K}] linear (amax, quantize, "
+                      f"dequantize, float64 GEMM, epilogue), weights pre-quantized; {dt:.2f} s",
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
@@ -285,7 +289,7 @@ def main():
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(lin.x, lin.w, args.cpu_rows)
+        rec["cpu_baseline"] = cpu_baseline(lin.x, lin.w, args.cpu_rows, args.cpu_repeats)
     print(json.dumps(rec), flush=True)
 
 
