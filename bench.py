@@ -277,8 +277,8 @@ def main():
         "quantize_ms": round(q_ms, 4),
         "quantize_hbm_frac": round(q_gbs / PEAK_HBM_GBS, 4),
         "quantize_traffic": None if q_traffic is None else round(q_traffic),
-        "roofline": {"kernel": "nvfp4_gemm: gemm_pipe_kernel<false> (1536 whole 256x256 tiles) + "
-                               "gemm_pipe_kernel<true> (64 tiles x 4 K splits) + split_k_reduce",
+        "roofline": {"kernel": "nvfp4_gemm: gemm_pipe_kernel<false, 4> (1536 whole 256x256 tiles) + "
+                               "gemm_pipe_kernel<true, 4> (64 tiles x 4 K splits) + split_k_reduce",
                      "bound": "mfma",
                      "achieved": round(g_tflops, 2), "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(g_tflops / PEAK_F16_MFMA_TFLOPS, 4),

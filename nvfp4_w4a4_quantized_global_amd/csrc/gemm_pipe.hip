@@ -40,20 +40,33 @@ namespace {
 
 using namespace gemm;
 
-constexpr int kRows = 256;                       // rows of A and of B per tile
-constexpr int kCodeBytes = kRows * 64;           // one operand's codes of one K tile
-constexpr int kScaleBytes = kRows * 8;           // one operand's scales of one K tile
-constexpr int kOffB = kCodeBytes;
-constexpr int kOffAS = 2 * kCodeBytes;
-constexpr int kOffBS = 2 * kCodeBytes + kScaleBytes;
-constexpr int kStage = 2 * kCodeBytes + 2 * kScaleBytes;   // 36 KB
+constexpr int kRows = 256;                       // rows of B (output columns) per tile
 constexpr int kEpiRowBytes = 128 * 2 + 16;
-constexpr int kLds = 2 * kStage;                            // 72 KB
-static_assert(4 * 32 * kEpiRowBytes <= kLds, "epilogue staging fits in the stages");
+
+// Tile geometry for kTM 32-row MFMA tiles per wave along M (2 x 2 waves): A rows per
+// tile 64 * kTM (256, or 128 for few activation rows), B rows 256.  One LDS stage holds
+// a K tile of both operands: A codes, B codes, A scales, B scales.
+template <int kTM>
+struct Geo {
+  static constexpr int kRowsA = 64 * kTM;
+  static constexpr int kOffB = kRowsA * 64;
+  static constexpr int kOffAS = kOffB + kRows * 64;
+  static constexpr int kOffBS = kOffAS + kRowsA * 8;
+  static constexpr int kStage = kOffBS + kRows * 8;    // 36 KB (kTM 4) or 27 KB (kTM 2)
+  static constexpr int kLds = 2 * kStage;
+  static constexpr int kAcc = kTM * 64;                // accumulator entries per thread
+  static_assert(4 * 32 * kEpiRowBytes <= kLds, "epilogue staging fits in the stages");
+};
 
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+// One 16-byte global -> LDS copy per lane.  A plain function, so that the target
+// builtin is never part of a template-dependent expression.
+__device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+}
 
 // Tile index -> (tile row, tile column): bands of kGroupM tile rows, N-major inside a
 // band, so consecutive indices (the tiles resident on one XCD at a time) cover a
@@ -73,10 +86,10 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int kMem>
-__device__ __forceinline__ void interleave16() {
+template <int kMem, int kN>
+__device__ __forceinline__ void interleave() {
 #pragma unroll
-  for (int g = 0; g < 16; ++g) {
+  for (int g = 0; g < kN; ++g) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // one MFMA
     if (kMem != 0) __builtin_amdgcn_sched_group_barrier(kMem, 1, 0);   // one memory op
     __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);                 // a few VALU
@@ -86,7 +99,8 @@ __device__ __forceinline__ void interleave16() {
 
 // kSplit: the launch for the tiles past the last whole round, each split along K into
 // fp32 partials (`splits` blocks per tile); otherwise whole tiles with the epilogue.
-template <bool kSplit>
+// kTM: 32-row MFMA tiles per wave along M (4: 256 x 256 tiles, 2: 128 x 256).
+template <bool kSplit, int kTM>
 __global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m, int64_t k,
     const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, int64_t n,
@@ -95,6 +109,8 @@ __global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
     int tiles_n, int tile0, int splits,
     float* __restrict__ partial) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  using G = Geo<kTM>;
+  constexpr int kOffB = G::kOffB, kOffAS = G::kOffAS, kOffBS = G::kOffBS, kStage = G::kStage;
   // Tile indices follow tile_coords.  Without split-K, workgroups (dealt round-robin to
   // the 8 XCDs) are remapped so each XCD gets a contiguous run of tile indices, whose
   // resident tiles then share operand panels in its L2.  With split-K, block b takes K
@@ -111,7 +127,7 @@ __global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
   bid += tile0;
   int tm, tn;
   tile_coords(bid, tiles_m, tiles_n, tm, tn);
-  const int64_t row0 = (int64_t)tm * kRows;
+  const int64_t row0 = (int64_t)tm * G::kRowsA;
   const int64_t col0 = (int64_t)tn * kRows;
 
   const int t = threadIdx.x;
@@ -126,20 +142,27 @@ __global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
   const int64_t kt_begin = kt_all * split / nsplit;        // this block's K tiles
   const int64_t kt_end = kt_all * (split + 1) / nsplit;
 
-  // Direct loads: wave w, instruction i fills LDS rows 16*(4w+i) .. +15 of an operand;
-  // lane l lands in slot (l & 3) of row 16*(4w+i) + l/4 and so fetches logical chunk
-  // (l & 3) ^ swz(row).
-  const uint8_t* ag[4];
+  // Direct loads: for B, wave w, instruction i fills LDS rows 16*(4w+i) .. +15; for A,
+  // rows 16*(kTM w+i) .. +15.  Lane l lands in slot (l & 3) of row (base + l/4) and so
+  // fetches logical chunk (l & 3) ^ swz(row).
+  const uint8_t* ag[kTM];
   const uint8_t* bg[4];
-  int chunk[4];
+  int chunk_a[kTM], chunk_b[4];
+#pragma unroll
+  for (int i = 0; i < kTM; ++i) {
+    const int r = 16 * (kTM * wave + i) + (lane >> 2);
+    chunk_a[i] = (lane & 3) ^ swz(r);
+    ag[i] = a_codes + min(row0 + r, m - 1) * half_k + 16 * chunk_a[i];
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 16 * (4 * wave + i) + (lane >> 2);
-    chunk[i] = (lane & 3) ^ swz(r);
-    ag[i] = a_codes + min(row0 + r, m - 1) * half_k + 16 * chunk[i];
-    bg[i] = b_codes + min(col0 + r, n - 1) * half_k + 16 * chunk[i];
+    chunk_b[i] = (lane & 3) ^ swz(r);
+    bg[i] = b_codes + min(col0 + r, n - 1) * half_k + 16 * chunk_b[i];
   }
-  const uint8_t* asg = a_scales + min(row0 + t, m - 1) * 8;
+  // the threads that move A's scale rows: all 256 for 256-row tiles (a constant there)
+  const bool a_scale_thread = G::kRowsA >= 256 || t < G::kRowsA;
+  const uint8_t* asg = a_scales + min(row0 + (a_scale_thread ? t : 0), m - 1) * 8;
   const uint8_t* bsg = b_scales + min(col0 + t, n - 1) * 8;
 
   auto stage = [&](int64_t kt) { return lds + (int)(kt & 1) * kStage; };
@@ -153,13 +176,14 @@ __global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
     uint8_t* st = stage(kt);
     const int64_t off = min(kt, kt_end - 1) * 64;
 #pragma unroll
+    for (int i = 0; i < kTM; ++i) {
+      const bool in_row = off + 16 * chunk_a[i] < half_k;
+      dma16(ag[i] + (in_row ? off : -16 * chunk_a[i]), st + (kTM * wave + i) * 1024);
+    }
+#pragma unroll
     for (int i = 0; i < 4; ++i) {
-      lds_void* la = (lds_void*)(st + (4 * wave + i) * 1024);
-      lds_void* lb = (lds_void*)(st + kOffB + (4 * wave + i) * 1024);
-      const bool in_row = off + 16 * chunk[i] < half_k;
-      const int64_t o = in_row ? off : -16 * chunk[i];
-      __builtin_amdgcn_global_load_lds(ag[i] + o, la, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(bg[i] + o, lb, 16, 0, 0);
+      const bool in_row = off + 16 * chunk_b[i] < half_k;
+      dma16(bg[i] + (in_row ? off : -16 * chunk_b[i]), st + kOffB + (4 * wave + i) * 1024);
     }
   };
   uint2 sa_reg, sb_reg;
@@ -170,22 +194,22 @@ __global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
   };
   auto sstore_scales = [&](int64_t kt) {
     uint8_t* st = stage(kt);
-    *reinterpret_cast<uint2*>(st + kOffAS + t * 8) = sa_reg;
+    if (a_scale_thread) *reinterpret_cast<uint2*>(st + kOffAS + t * 8) = sa_reg;
     *reinterpret_cast<uint2*>(st + kOffBS + t * 8) = sb_reg;
   };
 
-  const int arow = wm * 128 + lr;
+  const int arow = wm * (32 * kTM) + lr;
   const int brow = wn * 128 + lr;
-  auto rscale = [&](const uint8_t* st, uint32_t (&as)[4], uint32_t (&bs)[4]) {
+  auto rscale = [&](const uint8_t* st, uint32_t (&as)[kTM], uint32_t (&bs)[4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) as[i] = *reinterpret_cast<const uint32_t*>(st + kOffAS + (arow + 32 * i) * 8 + 4 * kh);
+    for (int i = 0; i < kTM; ++i) as[i] = *reinterpret_cast<const uint32_t*>(st + kOffAS + (arow + 32 * i) * 8 + 4 * kh);
 #pragma unroll
     for (int j = 0; j < 4; ++j) bs[j] = *reinterpret_cast<const uint32_t*>(st + kOffBS + (brow + 32 * j) * 8 + 4 * kh);
   };
   // half q of the lane's 32 code bytes: logical chunk 2*kh + q
-  auto rhalf = [&](const uint8_t* st, int q, uint4 (&ar)[4], uint4 (&br)[4]) {
+  auto rhalf = [&](const uint8_t* st, int q, uint4 (&ar)[kTM], uint4 (&br)[4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kTM; ++i) {
       const int r = arow + 32 * i;
       ar[i] = *reinterpret_cast<const uint4*>(st + r * 64 + 16 * ((2 * kh + q) ^ swz(r)));
     }
@@ -195,24 +219,24 @@ __global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
       br[j] = *reinterpret_cast<const uint4*>(st + kOffB + r * 64 + 16 * ((2 * kh + q) ^ swz(r)));
     }
   };
-  auto expand = [&](const uint4 (&ar)[4], const uint4 (&br)[4], const uint32_t (&as)[4], const uint32_t (&bs)[4],
-                    int step, half8_t (&fa)[4], half8_t (&fb)[4]) {
+  auto expand = [&](const uint4 (&ar)[kTM], const uint4 (&br)[4], const uint32_t (&as)[kTM],
+                    const uint32_t (&bs)[4], int step, half8_t (&fa)[kTM], half8_t (&fb)[4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = dequant8(word(ar[i], step & 3), scale_pair(as[i], step >> 1));
+    for (int i = 0; i < kTM; ++i) fa[i] = dequant8(word(ar[i], step & 3), scale_pair(as[i], step >> 1));
 #pragma unroll
     for (int j = 0; j < 4; ++j) fb[j] = dequant8(word(br[j], step & 3), scale_pair(bs[j], step >> 1));
   };
 
-  float16_t acc[4][4];
+  float16_t acc[kTM][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kTM; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-  auto mfma16 = [&](const half8_t (&fa)[4], const half8_t (&fb)[4]) {
+  auto mfma16 = [&](const half8_t (&fa)[kTM], const half8_t (&fb)[4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kTM; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
   };
@@ -224,11 +248,11 @@ __global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
   gload_scales(kt_begin + 1);
   gload_codes(kt_begin + 1);
   stage_barrier();
-  uint32_t asc[4], bsc[4];
-  uint4 ar0[4], br0[4], ar1[4], br1[4];
+  uint32_t asc[kTM], bsc[4];
+  uint4 ar0[kTM], br0[4], ar1[kTM], br1[4];
   rscale(stage(kt_begin), asc, bsc);
   rhalf(stage(kt_begin), 0, ar0, br0);
-  half8_t fa[4], fb[4], na[4], nb[4];
+  half8_t fa[kTM], fb[4], na[kTM], nb[4];
   expand(ar0, br0, asc, bsc, 0, fa, fb);
 
   // Every iteration is the same branch-free body (the last two also prepare tiles that
@@ -240,55 +264,57 @@ __global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
     // sub-step 0
     expand(ar0, br0, asc, bsc, 1, na, nb);
     mfma16(fa, fb);
-    interleave16<0>();
+    interleave<0, 4 * kTM>();
     // sub-step 1
     expand(ar0, br0, asc, bsc, 2, fa, fb);
     mfma16(na, nb);
-    interleave16<0>();
+    interleave<0, 4 * kTM>();
     // sub-step 2
     rhalf(cur, 1, ar1, br1);
     expand(ar0, br0, asc, bsc, 3, na, nb);
     mfma16(fa, fb);
-    interleave16<0x100>();
+    interleave<0x100, 4 * kTM>();
     // sub-step 3
     expand(ar1, br1, asc, bsc, 4, fa, fb);
     mfma16(na, nb);
-    interleave16<0>();
+    interleave<0, 4 * kTM>();
     // sub-step 4: the next tile's scales (loaded a tile ago) go to its stage
     sstore_scales(kt + 1);
     expand(ar1, br1, asc, bsc, 5, na, nb);
     mfma16(fa, fb);
-    interleave16<0x200>();
+    interleave<0x200, 4 * kTM>();
     stage_barrier();
     // sub-step 5
-    uint32_t nasc[4], nbsc[4];
+    uint32_t nasc[kTM], nbsc[4];
     rscale(nxt, nasc, nbsc);
     rhalf(nxt, 0, ar0, br0);
     gload_scales(kt + 2);
     gload_codes(kt + 2);
     expand(ar1, br1, asc, bsc, 6, fa, fb);
     mfma16(na, nb);
-    interleave16<0x100>();
+    interleave<0x100, 4 * kTM>();
     // sub-step 6
     expand(ar1, br1, asc, bsc, 7, na, nb);
     mfma16(fa, fb);
-    interleave16<0>();
+    interleave<0, 4 * kTM>();
     // sub-step 7: the next tile's first fragments
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { asc[i] = nasc[i]; bsc[i] = nbsc[i]; }
+    for (int i = 0; i < kTM; ++i) asc[i] = nasc[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bsc[j] = nbsc[j];
     expand(ar0, br0, asc, bsc, 0, fa, fb);
     mfma16(na, nb);
-    interleave16<0>();
+    interleave<0, 4 * kTM>();
   }
   stage_barrier();   // no load still landing in LDS, every wave done with the stages
 
   if (kSplit) {
     // Split-K: the raw fp32 accumulators of this K range, in register order (entry q of
-    // thread t at ((split * tiles + tile) * 256 + q) * 256 + t); split_k_reduce finishes.
+    // thread t at ((split * tiles + tile) * kAcc + q) * 256 + t); split_k_reduce finishes.
     const int tiles = gridDim.x / splits;
-    float* p = partial + ((int64_t)split * tiles + blockIdx.x / splits) * 65536 + t;
+    float* p = partial + ((int64_t)split * tiles + blockIdx.x / splits) * (G::kAcc * 256) + t;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kTM; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -299,10 +325,10 @@ __global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
   // Epilogue: bf16(alpha * acc) staged through LDS 32 rows per wave at a time, then
   // bf16(y + bias), written as 16-byte row segments.
   uint8_t* epi = lds + wave * 32 * kEpiRowBytes;
-  const int64_t wrow0 = row0 + wm * 128;
+  const int64_t wrow0 = row0 + wm * (32 * kTM);
   const int64_t wcol0 = col0 + wn * 128;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kTM; ++i) {
     float al[16];
     group_alphas(gsf_a, gsf_b, a_seg_rows, wrow0 + i * 32, kh, m, al);
 #pragma unroll
@@ -348,24 +374,26 @@ __global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
 
 // Sums the split-K partials of `tiles` tiles (starting at tile index tile0) in split
 // order, then applies the epilogue of the main kernel: bf16(alpha * acc), then the bias.
+template <int kTM>
 __global__ void __launch_bounds__(256) split_k_reduce(const float* __restrict__ partial, int splits, int tiles,
                                                       int tile0, int tiles_m, int64_t m, int64_t n,
                                                       const float* __restrict__ gsf_a, const float* __restrict__ gsf_b,
                                                       int64_t a_seg_rows, const uint16_t* __restrict__ bias,
                                                       uint16_t* __restrict__ out, int64_t ldo) {
-  const int tl = blockIdx.x >> 8;         // tile within the split launch
-  const int q = blockIdx.x & 255;         // accumulator entry (i, j, e) of the owning thread
+  using G = Geo<kTM>;
+  const int tl = blockIdx.x / G::kAcc;    // tile within the split launch
+  const int q = blockIdx.x % G::kAcc;     // accumulator entry (i, j, e) of the owning thread
   const int t = threadIdx.x;              // owning thread of the main kernel
   float acc = 0.0f;
-  for (int sp = 0; sp < splits; ++sp) acc += partial[(((int64_t)sp * tiles + tl) * 256 + q) * 256 + t];
+  for (int sp = 0; sp < splits; ++sp) acc += partial[(((int64_t)sp * tiles + tl) * G::kAcc + q) * 256 + t];
   const int tile = tile0 + tl;
   int tm, tn;
   tile_coords(tile, tiles_m, (int)((n + kRows - 1) / kRows), tm, tn);
-  const int64_t row0 = (int64_t)tm * kRows;
+  const int64_t row0 = (int64_t)tm * G::kRowsA;
   const int64_t col0 = (int64_t)tn * kRows;
   const int wave = t >> 6, lane = t & 63;
   const int i = q >> 6, j = (q >> 4) & 3, e = q & 15;
-  const int64_t row = row0 + (wave >> 1) * 128 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+  const int64_t row = row0 + (wave >> 1) * (32 * kTM) + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
   const int64_t col = col0 + (wave & 1) * 128 + j * 32 + (lane & 31);
   if (row >= m || col >= n) return;
   const float alpha = alpha_for(gsf_a, gsf_b, a_seg_rows, row);
@@ -374,17 +402,26 @@ __global__ void __launch_bounds__(256) split_k_reduce(const float* __restrict__ 
   out[row * ldo + col] = (uint16_t)y;
 }
 
+// Few activation rows take 128-row tiles (half the MFMA work of a 256-row tile that
+// would mostly multiply clamped rows).
+int pipe_tm(int64_t m) { return m <= 128 ? 2 : 4; }
+
 // How a problem is cut: `full` tiles in whole rounds of one tile per compute unit,
 // then `rest` tiles, each split `splits` ways along K when that fills the GPU better
 // and the workspace allows it.
 struct PipePlan {
   int64_t tiles_m, tiles_n, full, rest;
   int splits;
+  int tm;                  // kTM of the kernel
+  size_t partial_floats;   // per split tile
 };
 
 PipePlan pipe_plan(int64_t m, int64_t k, int64_t n, int cus) {
   PipePlan p;
-  p.tiles_m = (m + kRows - 1) / kRows;
+  p.tm = pipe_tm(m);
+  const int64_t rows_a = 64 * p.tm;
+  p.partial_floats = (size_t)rows_a * kRows;
+  p.tiles_m = (m + rows_a - 1) / rows_a;
   p.tiles_n = (n + kRows - 1) / kRows;
   const int64_t tiles = p.tiles_m * p.tiles_n;
   p.full = tiles / cus * cus;
@@ -399,6 +436,51 @@ PipePlan pipe_plan(int64_t m, int64_t k, int64_t n, int cus) {
   return p;
 }
 
+size_t plan_bytes(const PipePlan& p) {
+  return p.splits > 1 ? (size_t)p.splits * (size_t)p.rest * p.partial_floats * sizeof(float) : 0;
+}
+
+template <int kTM>
+hipError_t launch_plan(const PipePlan& p, const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, int64_t k,
+                       const uint8_t* b_codes, const uint8_t* b_scales, int64_t n, const float* gsf_a,
+                       const float* gsf_b, int64_t a_seg_rows, const uint16_t* bias, uint16_t* out, float* partial,
+                       hipStream_t s) {
+  constexpr int kLds = Geo<kTM>::kLds;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_pipe_kernel<false, kTM>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_pipe_kernel<true, kTM>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int tm = (int)p.tiles_m, tn = (int)p.tiles_n;
+  if (p.full > 0) {
+    hipLaunchKernelGGL((gemm_pipe_kernel<false, kTM>), dim3((uint32_t)p.full), dim3(256), kLds, s, a_codes, a_scales,
+                       m, k, b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, n, n, tm, tn, 0, 1,
+                       (float*)nullptr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.rest == 0) return hipSuccess;
+  if (p.splits == 1) {
+    hipLaunchKernelGGL((gemm_pipe_kernel<false, kTM>), dim3((uint32_t)p.rest), dim3(256), kLds, s, a_codes, a_scales,
+                       m, k, b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, n, n, tm, tn, (int)p.full, 1,
+                       (float*)nullptr);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((gemm_pipe_kernel<true, kTM>), dim3((uint32_t)(p.rest * p.splits)), dim3(256), kLds, s, a_codes,
+                     a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, n, n, tm, tn,
+                     (int)p.full, p.splits, partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((split_k_reduce<kTM>), dim3((uint32_t)(p.rest * Geo<kTM>::kAcc)), dim3(256), 0, s, partial,
+                     p.splits, (int)p.rest, (int)p.full, tm, m, n, gsf_a, gsf_b, a_seg_rows, bias, out, n);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool gemm_pipe_supported(int64_t m, int64_t k, int64_t n, const void* a_codes, const void* a_scales,
@@ -411,49 +493,22 @@ bool gemm_pipe_supported(int64_t m, int64_t k, int64_t n, const void* a_codes, c
 }
 
 size_t gemm_pipe_workspace_bytes(int64_t m, int64_t k, int64_t n, int cus) {
-  const PipePlan p = pipe_plan(m, k, n, cus);
-  return p.splits > 1 ? (size_t)p.splits * (size_t)p.rest * 65536u * sizeof(float) : 0;
+  return plan_bytes(pipe_plan(m, k, n, cus));
 }
 
 hipError_t launch_gemm_pipe(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, int64_t k,
                             const uint8_t* b_codes, const uint8_t* b_scales, int64_t n, const float* gsf_a,
                             const float* gsf_b, int64_t a_seg_rows, const uint16_t* bias, uint16_t* out,
                             void* workspace, size_t workspace_bytes, int cus, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_pipe_kernel<false>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_pipe_kernel<true>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   PipePlan p = pipe_plan(m, k, n, cus);
-  const size_t need = p.splits > 1 ? (size_t)p.splits * (size_t)p.rest * 65536u * sizeof(float) : 0;
+  const size_t need = plan_bytes(p);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) p.splits = 1;
-  const int tm = (int)p.tiles_m, tn = (int)p.tiles_n;
-  if (p.full > 0) {
-    hipLaunchKernelGGL(gemm_pipe_kernel<false>, dim3((uint32_t)p.full), dim3(256), kLds, s, a_codes, a_scales, m, k, b_codes,
-                       b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, n, n, tm, tn, 0, 1, (float*)nullptr);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (p.rest == 0) return hipSuccess;
   float* partial = static_cast<float*>(workspace);
-  if (p.splits == 1) {
-    hipLaunchKernelGGL(gemm_pipe_kernel<false>, dim3((uint32_t)p.rest), dim3(256), kLds, s, a_codes, a_scales, m, k,
-                       b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, n, n, tm, tn, (int)p.full, 1, (float*)nullptr);
-    return hipGetLastError();
-  }
-  hipLaunchKernelGGL(gemm_pipe_kernel<true>, dim3((uint32_t)(p.rest * p.splits)), dim3(256), kLds, s, a_codes,
-                     a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, n, n, tm, tn, (int)p.full,
-                     p.splits, partial);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(split_k_reduce, dim3((uint32_t)(p.rest * 256)), dim3(256), 0, s, partial, p.splits, (int)p.rest,
-                     (int)p.full, tm, m, n, gsf_a, gsf_b, a_seg_rows, bias, out, n);
-  return hipGetLastError();
+  if (p.tm == 2)
+    return launch_plan<2>(p, a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out,
+                          partial, s);
+  return launch_plan<4>(p, a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out,
+                        partial, s);
 }
 
 }  // namespace nvfp4

@@ -207,10 +207,12 @@ def test_few_rows_weight_streaming(m, n, k):
     assert_gemm_close(whole.float().cpu().numpy(), ref, bound)
 
 
-@pytest.mark.parametrize("m,n,k", [(65, 4352, 1056), (200, 4100, 2080), (511, 1000, 640), (128, 25600, 512)])
+@pytest.mark.parametrize("m,n,k", [(65, 4352, 1056), (200, 4100, 2080), (511, 1000, 640), (128, 25600, 512),
+                                   (100, 65800, 256)])
 def test_mid_rows_pipelined_split(m, n, k):
-    """Between the decode and the full-tile shapes: the pipelined kernel on a single
-    row of ragged 256x256 tiles, split along K up to one tile per compute unit."""
+    """Between the decode and the full-tile shapes: the pipelined kernel on ragged
+    128x256 (M <= 128) or 256x256 tiles, split along K up to one tile per compute
+    unit; the last case fills a whole round of 128-row tiles and leaves two more."""
     rng = np.random.default_rng(m + 3 * n + k)
     px, sx = random_operands(rng, m, k)
     pw, sw = random_operands(rng, n, k)
