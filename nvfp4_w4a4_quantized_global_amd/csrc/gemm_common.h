@@ -47,9 +47,13 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int s) {
 }
 
 // alpha = fp32(1 / fp32(gsf_a * gsf_b)).  With seg_rows > 0 the activation rows come in
-// blocks of seg_rows rows with one global scale each, gsf_a[row / seg_rows].
+// blocks of seg_rows rows with one global scale each, gsf_a[row / seg_rows].  Rows and
+// seg_rows are below 2^31 (the C ABI rejects larger), so the division is a 32-bit one.
+__device__ __forceinline__ uint32_t segment_of(int64_t row, int64_t seg_rows) {
+  return (uint32_t)row / (uint32_t)seg_rows;
+}
 __device__ __forceinline__ float alpha_for(const float* gsf_a, const float* gsf_b, int64_t seg_rows, int64_t row) {
-  const float ga = seg_rows > 0 ? gsf_a[row / seg_rows] : *gsf_a;
+  const float ga = seg_rows > 0 ? gsf_a[segment_of(row, seg_rows)] : *gsf_a;
   return __fdiv_rn(1.0f, __fmul_rn(ga, *gsf_b));
 }
 
@@ -60,7 +64,7 @@ __device__ __forceinline__ void group_alphas(const float* gsf_a, const float* gs
                                              int kh, int64_t m, float (&al)[16]) {
   const int64_t first = g0 < m - 1 ? g0 : m - 1;
   const int64_t last = g0 + 31 < m - 1 ? g0 + 31 : m - 1;
-  if (seg_rows <= 0 || first / seg_rows == last / seg_rows) {
+  if (seg_rows <= 0 || segment_of(first, seg_rows) == segment_of(last, seg_rows)) {
     const float a = alpha_for(gsf_a, gsf_b, seg_rows, first);
 #pragma unroll
     for (int e = 0; e < 16; ++e) al[e] = a;
@@ -71,6 +75,14 @@ __device__ __forceinline__ void group_alphas(const float* gsf_a, const float* gs
       al[e] = alpha_for(gsf_a, gsf_b, seg_rows, r < m - 1 ? r : m - 1);
     }
   }
+}
+
+// Two fp32 values -> two bf16, nearest even (v_cvt_pk_bf16_f32; the same bits as
+// f32_to_bf16 for every finite value), a in the low half.
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){a, b}, bf16x2_t));
 }
 
 // bf16(y) + bias in fp32, rounded to bf16: the bias add after the GEMM output is rounded.

@@ -81,6 +81,10 @@ __device__ __forceinline__ void tile_coords(int tile, int tiles_m, int tiles_n, 
   tn = in_band / rows;
 }
 
+// Orders this wave's LDS accesses around a point: everything before it has completed,
+// and the compiler moves no memory access across it.
+__device__ __forceinline__ void lds_order() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // Waits for this wave's global and LDS traffic, then the workgroup barrier.
 __device__ __forceinline__ void stage_barrier() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -227,6 +231,10 @@ __global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
     for (int j = 0; j < 4; ++j) fb[j] = dequant8(word(br[j], step & 3), scale_pair(bs[j], step >> 1));
   };
 
+  // acc[i][j] is the 32 x 32 output block (rows 32 i, columns 32 j of the wave's
+  // quarter), computed as the transposed product (weight fragments as the MFMA's first
+  // operand): entry e of lane l is output row l % 32, column 8 (e / 4) + 4 (l / 32) + e % 4,
+  // so each lane holds runs of 4 consecutive columns of one row.
   float16_t acc[kTM][4];
 #pragma unroll
   for (int i = 0; i < kTM; ++i)
@@ -238,7 +246,7 @@ __global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
   };
 
   // Prologue: the first K tile complete in its stage, the second in flight.
@@ -322,58 +330,88 @@ __global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
     return;
   }
 
-  // Epilogue: bf16(alpha * acc) staged through LDS 32 rows per wave at a time, then
-  // bf16(y + bias), written as 16-byte row segments.
+  // Epilogue: bf16(alpha * acc) staged through LDS 32 rows per wave at a time (8-byte
+  // writes of 4 consecutive columns), then bf16(y + bias), written as 16-byte row
+  // segments.  Each wave stages its own rows in its own LDS region, so only the wave's
+  // own LDS order matters between the writes and the reads (lds_order): no workgroup
+  // barrier, and nothing waits for the global stores, which drain while the workgroup
+  // ends and the next one starts.
   uint8_t* epi = lds + wave * 32 * kEpiRowBytes;
   const int64_t wrow0 = row0 + wm * (32 * kTM);
   const int64_t wcol0 = col0 + wn * 128;
+  // Lane l always stores the 8 columns col = wcol0 + 8 (l % 16) .. +7: it loads their
+  // bias once, and stores them as one 16-byte segment when they are all inside the
+  // output and the row starts are 16-byte aligned.
+  const int64_t col = wcol0 + 8 * (lane & 15);
+  const bool vec_store = col + 8 <= n && (ldo & 7) == 0 && ((uintptr_t)out & 15) == 0;
+  uint32_t bw[4] = {0, 0, 0, 0};
+  if (bias != nullptr) {
+    if (col + 8 <= n && ((uintptr_t)(bias + col) & 15) == 0) {
+      const uint4 v = *reinterpret_cast<const uint4*>(bias + col);
+      bw[0] = v.x;
+      bw[1] = v.y;
+      bw[2] = v.z;
+      bw[3] = v.w;
+    } else {
+#pragma unroll
+      for (int h = 0; h < 8; ++h)
+        if (col + h < n) bw[h >> 1] |= (uint32_t)bias[col + h] << (16 * (h & 1));
+    }
+  }
+  const float alpha0 = a_seg_rows > 0 ? 0.0f : alpha_for(gsf_a, gsf_b, 0, 0);
 #pragma unroll
   for (int i = 0; i < kTM; ++i) {
-    float al[16];
-    group_alphas(gsf_a, gsf_b, a_seg_rows, wrow0 + i * 32, kh, m, al);
+    const int64_t arow = wrow0 + i * 32 + lr;    // this lane's accumulator row
+    const float al = a_seg_rows > 0 ? alpha_for(gsf_a, gsf_b, a_seg_rows, min(arow, m - 1)) : alpha0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int r = 8 * (e >> 2) + 4 * kh + (e & 3);
-        const float y = __fmul_rn(al[e], __fmul_rn(acc[i][j][e], kAccUnscale));
-        *reinterpret_cast<uint16_t*>(epi + r * kEpiRowBytes + (j * 32 + lr) * 2) = (uint16_t)f32_to_bf16(y);
+      for (int q = 0; q < 4; ++q) {
+        float y[4];
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) y[s4] = __fmul_rn(al, __fmul_rn(acc[i][j][4 * q + s4], kAccUnscale));
+        *reinterpret_cast<uint2*>(epi + lr * kEpiRowBytes + (32 * j + 8 * q + 4 * kh) * 2) =
+            make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
       }
     }
-    __syncthreads();
+    lds_order();
+    const int64_t row_i = wrow0 + i * 32 + (lane >> 4);
+    uint16_t* const out_i = out + row_i * ldo + col;
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
-      const int idx = p * 64 + lane;
-      const int r = idx >> 4, sg = idx & 15;
-      const int64_t row = wrow0 + i * 32 + r;
-      const int64_t col = wcol0 + sg * 8;
-      const uint4 v = *reinterpret_cast<const uint4*>(epi + r * kEpiRowBytes + sg * 16);
-      if (row < m && col < n) {
-        uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        if (bias != nullptr) {
+      const int r = 4 * p + (lane >> 4);
+      const int64_t row = row_i + 4 * p;
+      const uint4 v = *reinterpret_cast<const uint4*>(epi + r * kEpiRowBytes + (lane & 15) * 16);
+      uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      if (bias != nullptr) {
 #pragma unroll
-          for (int h = 0; h < 8; ++h) {
-            if (col + h < n) {
-              const uint32_t sh = 16 * (h & 1);
-              const uint32_t zb = add_bias_bf16((w[h >> 1] >> sh) & 0xFFFFu, bias[col + h]);
-              w[h >> 1] = (w[h >> 1] & (0xFFFF0000u >> sh)) | (zb << sh);
-            }
-          }
+        for (int h = 0; h < 8; ++h) {
+          const uint32_t sh = 16 * (h & 1);
+          const uint32_t zb = add_bias_bf16((w[h >> 1] >> sh) & 0xFFFFu, (uint16_t)(bw[h >> 1] >> sh));
+          w[h >> 1] = (w[h >> 1] & (0xFFFF0000u >> sh)) | (zb << sh);
         }
-        uint16_t* o = out + row * ldo + col;
-        if (col + 8 <= n && ((uintptr_t)o & 15) == 0) {
+      }
+      if (row < m) {
+        uint16_t* o = out_i + 4 * p * ldo;
+        if (vec_store) {
           *reinterpret_cast<uint4*>(o) = make_uint4(w[0], w[1], w[2], w[3]);
-        } else {
-          for (int h = 0; h < 8 && col + h < n; ++h) o[h] = (uint16_t)((w[h >> 1] >> (16 * (h & 1))) & 0xFFFFu);
+        } else if (col < n) {
+          const uint64_t lo = ((uint64_t)w[1] << 32) | w[0], hi = ((uint64_t)w[3] << 32) | w[2];
+          const int cnt = n - col < 8 ? (int)(n - col) : 8;
+#pragma unroll 1
+          for (int h = 0; h < cnt; ++h) o[h] = (uint16_t)((h < 4 ? lo : hi) >> (16 * (h & 3)));
         }
       }
     }
-    __syncthreads();
+    lds_order();
   }
 }
 
 // Sums the split-K partials of `tiles` tiles (starting at tile index tile0) in split
 // order, then applies the epilogue of the main kernel: bf16(alpha * acc), then the bias.
+// Each thread finishes 8 consecutive columns of one output row: entries 4 q' .. 4 q' + 3
+// of accumulator block (i, j) of the main kernel's lanes l and l + 32 (l < 32) of one
+// wave; consecutive threads take consecutive l, so the partial reads coalesce.
 template <int kTM>
 __global__ void __launch_bounds__(256) split_k_reduce(const float* __restrict__ partial, int splits, int tiles,
                                                       int tile0, int tiles_m, int64_t m, int64_t n,
@@ -381,25 +419,64 @@ __global__ void __launch_bounds__(256) split_k_reduce(const float* __restrict__ 
                                                       int64_t a_seg_rows, const uint16_t* __restrict__ bias,
                                                       uint16_t* __restrict__ out, int64_t ldo) {
   using G = Geo<kTM>;
-  const int tl = blockIdx.x / G::kAcc;    // tile within the split launch
-  const int q = blockIdx.x % G::kAcc;     // accumulator entry (i, j, e) of the owning thread
-  const int t = threadIdx.x;              // owning thread of the main kernel
-  float acc = 0.0f;
-  for (int sp = 0; sp < splits; ++sp) acc += partial[(((int64_t)sp * tiles + tl) * G::kAcc + q) * 256 + t];
+  constexpr int kPerTile = G::kAcc * 256 / 8;     // threads per tile
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int tl = (int)(gid / kPerTile);            // tile within the split launch
+  int u = (int)(gid % kPerTile);
+  const int l = u & 31;
+  u >>= 5;
+  const int qq = u & 3;
+  u >>= 2;
+  const int j = u & 3;
+  u >>= 2;
+  const int i = u % kTM;
+  const int wave = u / kTM;
+  // value h of split sp: entry (i * 4 + j) * 16 + 4 qq + h % 4 of thread 64 wave + 32 (h / 4) + l
+  const float* src = partial + ((int64_t)tl * G::kAcc + (i * 4 + j) * 16 + 4 * qq) * 256 + wave * 64 + l;
+  const int64_t split_stride = (int64_t)tiles * G::kAcc * 256;
+  auto load8 = [&](int sp, float (&v)[8]) {
+#pragma unroll
+    for (int h = 0; h < 8; ++h) v[h] = src[sp * split_stride + (h & 3) * 256 + 32 * (h >> 2)];
+  };
+  // Sums in split order; four splits' loads are in flight at a time.
+  float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  int sp = 0;
+  for (; sp + 4 <= splits; sp += 4) {
+    float v[4][8];
+#pragma unroll
+    for (int u4 = 0; u4 < 4; ++u4) load8(sp + u4, v[u4]);
+#pragma unroll
+    for (int u4 = 0; u4 < 4; ++u4)
+#pragma unroll
+      for (int h = 0; h < 8; ++h) acc[h] += v[u4][h];
+  }
+  for (; sp < splits; ++sp) {
+    float v[8];
+    load8(sp, v);
+#pragma unroll
+    for (int h = 0; h < 8; ++h) acc[h] += v[h];
+  }
   const int tile = tile0 + tl;
   int tm, tn;
   tile_coords(tile, tiles_m, (int)((n + kRows - 1) / kRows), tm, tn);
-  const int64_t row0 = (int64_t)tm * G::kRowsA;
-  const int64_t col0 = (int64_t)tn * kRows;
-  const int wave = t >> 6, lane = t & 63;
-  const int i = q >> 6, j = (q >> 4) & 3, e = q & 15;
-  const int64_t row = row0 + (wave >> 1) * (32 * kTM) + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-  const int64_t col = col0 + (wave & 1) * 128 + j * 32 + (lane & 31);
+  const int64_t row = (int64_t)tm * G::kRowsA + (wave >> 1) * (32 * kTM) + i * 32 + l;
+  const int64_t col = (int64_t)tn * kRows + (wave & 1) * 128 + j * 32 + 8 * qq;
   if (row >= m || col >= n) return;
   const float alpha = alpha_for(gsf_a, gsf_b, a_seg_rows, row);
-  uint32_t y = f32_to_bf16(__fmul_rn(alpha, __fmul_rn(acc, kAccUnscale)));
-  if (bias != nullptr) y = add_bias_bf16(y, bias[col]);
-  out[row * ldo + col] = (uint16_t)y;
+  uint16_t y[8];
+#pragma unroll
+  for (int h = 0; h < 8; ++h) {
+    uint32_t v = f32_to_bf16(__fmul_rn(alpha, __fmul_rn(acc[h], kAccUnscale)));
+    if (bias != nullptr && col + h < n) v = add_bias_bf16(v, bias[col + h]);
+    y[h] = (uint16_t)v;
+  }
+  uint16_t* o = out + row * ldo + col;
+  if (col + 8 <= n && ((uintptr_t)o & 15) == 0) {
+    *reinterpret_cast<uint4*>(o) = make_uint4(y[0] | ((uint32_t)y[1] << 16), y[2] | ((uint32_t)y[3] << 16),
+                                              y[4] | ((uint32_t)y[5] << 16), y[6] | ((uint32_t)y[7] << 16));
+  } else {
+    for (int h = 0; h < 8 && col + h < n; ++h) o[h] = y[h];
+  }
 }
 
 // Few activation rows take 128-row tiles (half the MFMA work of a 256-row tile that
@@ -476,7 +553,7 @@ hipError_t launch_plan(const PipePlan& p, const uint8_t* a_codes, const uint8_t*
                      (int)p.full, p.splits, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((split_k_reduce<kTM>), dim3((uint32_t)(p.rest * Geo<kTM>::kAcc)), dim3(256), 0, s, partial,
+  hipLaunchKernelGGL((split_k_reduce<kTM>), dim3((uint32_t)(p.rest * Geo<kTM>::kAcc / 8)), dim3(256), 0, s, partial,
                      p.splits, (int)p.rest, (int)p.full, tm, m, n, gsf_a, gsf_b, a_seg_rows, bias, out, n);
   return hipGetLastError();
 }
