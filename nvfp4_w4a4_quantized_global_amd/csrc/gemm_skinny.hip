@@ -19,6 +19,8 @@
 // permutation of K), so each lane loads 32 contiguous code bytes per row and the 16
 // lanes of a row together read its whole 128-byte line.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <stdint.h>
 
 #include "gemm_common.h"
@@ -247,13 +249,151 @@ __global__ void __launch_bounds__(256) gemm_skinny_reduce(const float* __restric
   out[idx] = (uint16_t)y;
 }
 
-// Block-level K splits: enough blocks for about two per compute unit, each block keeping
-// at least one 256-wide super tile per wave.
+// Block-level K splits: at most two blocks per compute unit (the kernel's registers
+// allow two resident), so all blocks run in one round, each block keeping at least one
+// 256-wide super tile per wave.
 int skinny_splits(int64_t k, int64_t n, int cus) {
   const int64_t groups = (n + kCols - 1) / kCols;
   const int64_t st = ((k + BK - 1) / BK + 1) / 2;
-  int64_t sp = (2 * cus + groups - 1) / groups;
+  int64_t sp = (2 * cus) / groups;
   const int64_t max_sp = st / kWaves > 0 ? st / kWaves : 1;
+  if (sp > max_sp) sp = max_sp;
+  return (int)(sp < 1 ? 1 : sp);
+}
+
+// Decode (m <= 16): a block owns 16 weight rows (one MFMA column tile) and a K range
+// whose 256-wide super tiles its four waves split into four consecutive quarters.  The
+// weight is read in whole 128-byte lines: each load instruction covers 8 rows of one
+// super tile (lane l: row l / 8, 16-byte chunk l % 8), so at any time a block streams
+// four sequential runs through 16 consecutive rows.  The lines go through a per-wave
+// LDS buffer into the MFMA layout (lane (n, g): row n, bytes 32 g .. 32 g + 31 of the
+// super tile; chunk c of row r sits in slot c ^ ((r / 2) % 8), which keeps both the
+// writes and the reads free of bank conflicts).  kDecDepth super tiles per wave are in
+// flight in registers.  The waves' sums are added through LDS in wave order; with a
+// block-level K split, fp32 partials go to gemm_skinny_reduce.
+constexpr int kDecRows = 16;
+constexpr int kDecDepth = 4;
+
+__device__ __forceinline__ int dec_swz(int r) { return (r >> 1) & 7; }
+
+__global__ void __launch_bounds__(256) gemm_decode_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m, int64_t k,
+    const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, int64_t n,
+    const float* __restrict__ gsf_a, const float* __restrict__ gsf_b, int64_t a_seg_rows,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int splits, float* __restrict__ partial) {
+  __shared__ __attribute__((aligned(16))) uint8_t buf[kWaves][kDecRows * 128];
+  __shared__ float red[kWaves - 1][4][64];
+
+  const int tile = blockIdx.x / splits;
+  const int split = blockIdx.x % splits;
+  const int64_t n0 = (int64_t)tile * kDecRows;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+  const int64_t half_k = k / 2;
+  const int64_t kt_all = (k + BK - 1) / BK;
+  const int64_t st_all = (kt_all + 1) / 2;
+  const int64_t b0 = st_all * split / splits, b1 = st_all * (split + 1) / splits;
+  const int64_t s0 = b0 + (b1 - b0) * wave / kWaves, s1 = b0 + (b1 - b0) * (wave + 1) / kWaves;
+  const int count = (int)(s1 - s0);
+
+  // line loads: rows lr and lr + 8 of the tile, logical chunk lc (lands in slot lane % 8)
+  const int lr = lane >> 3;
+  const int lc0 = (lane & 7) ^ dec_swz(lr), lc1 = (lane & 7) ^ dec_swz(lr + 8);
+  const uint8_t* bl0 = b_codes + min(n0 + lr, n - 1) * half_k + 16 * lc0;
+  const uint8_t* bl1 = b_codes + min(n0 + lr + 8, n - 1) * half_k + 16 * lc1;
+  const int64_t nb = min(n0 + l16, n - 1);                    // this lane's MFMA column
+  const uint8_t* bs_row = b_scales + nb * 8 + 4 * (g & 1);
+  const int64_t ra = min((int64_t)l16, m - 1);                 // this lane's MFMA row of A
+  const uint8_t* a_row = a_codes + ra * half_k + 32 * g;
+  const uint8_t* as_row = a_scales + ra * 8 + 4 * (g & 1);
+
+  struct Item {
+    uint4 b0, b1;       // two line chunks of the weight
+    uint4 a0, a1;       // this lane's 32 code bytes of A
+    uint32_t bs, as;    // the scale bytes of this lane's four 16-blocks
+  };
+  auto fetch = [&](int64_t st, Item& it) {
+    const int64_t off = st * 128;
+    const int64_t kt = 2 * st + (g >> 1);
+    const bool v0 = off + 16 * lc0 < half_k, v1 = off + 16 * lc1 < half_k;   // partial last super tile
+    it.b0 = v0 ? *reinterpret_cast<const uint4*>(bl0 + off) : make_uint4(0, 0, 0, 0);
+    it.b1 = v1 ? *reinterpret_cast<const uint4*>(bl1 + off) : make_uint4(0, 0, 0, 0);
+    const int64_t ao = off + 32 * g;
+    const bool c0 = ao < half_k, c1 = ao + 16 < half_k, sv = kt < kt_all;
+    it.a0 = c0 ? *reinterpret_cast<const uint4*>(a_row + off) : make_uint4(0, 0, 0, 0);
+    it.a1 = c1 ? *reinterpret_cast<const uint4*>(a_row + off + 16) : make_uint4(0, 0, 0, 0);
+    it.bs = sv ? *reinterpret_cast<const uint32_t*>(bs_row + kt * n * 8) : 0u;
+    it.as = sv ? *reinterpret_cast<const uint32_t*>(as_row + kt * m * 8) : 0u;
+  };
+  float4_t acc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  uint8_t* wb = buf[wave];
+  auto process = [&](const Item& it) {
+    // the wave's 16 rows x 128 bytes into LDS, then this lane's 32 bytes of row l16 back
+    *reinterpret_cast<uint4*>(wb + 16 * lane) = it.b0;
+    *reinterpret_cast<uint4*>(wb + 1024 + 16 * lane) = it.b1;
+    const uint4 w0 = *reinterpret_cast<const uint4*>(wb + l16 * 128 + 16 * ((2 * g) ^ dec_swz(l16)));
+    const uint4 w1 = *reinterpret_cast<const uint4*>(wb + l16 * 128 + 16 * ((2 * g + 1) ^ dec_swz(l16)));
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {                     // K values [64g + 8s, +8): block s/2
+      const half8_t fb = dequant8(word(s < 4 ? w0 : w1, s & 3), scale_pair(it.bs, s >> 1));
+      const half8_t fa = dequant8(word(s < 4 ? it.a0 : it.a1, s & 3), scale_pair(it.as, s >> 1));
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fb, acc, 0, 0, 0);
+    }
+  };
+  Item ring[kDecDepth];
+#pragma unroll
+  for (int u = 0; u < kDecDepth; ++u)
+    if (u < count) fetch(s0 + u, ring[u]);
+  for (int t = 0; t < count; t += kDecDepth) {
+#pragma unroll
+    for (int u = 0; u < kDecDepth; ++u) {
+      if (t + u < count) {
+        process(ring[u]);
+        if (t + u + kDecDepth < count) fetch(s0 + t + u + kDecDepth, ring[u]);
+      }
+    }
+  }
+
+  // Sum the four waves' K quarters in wave order: ((w0 + w1) + w2) + w3.
+  if (wave > 0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[wave - 1][e][lane] = acc[e];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < kWaves - 1; ++w)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += red[w][e][lane];
+
+  // 16x16 MFMA output: lane holds column l16, rows 4g .. 4g+3.
+  const int64_t col = n0 + l16;
+  if (col >= n) return;
+  const float alpha = __fdiv_rn(1.0f, __fmul_rn(*gsf_a, *gsf_b));   // one activation scale
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int64_t row = 4 * g + e;
+    if (row >= m) continue;
+    if (splits > 1) {
+      partial[((int64_t)split * m + row) * n + col] = acc[e];
+    } else {
+      const float al = a_seg_rows > 0 ? alpha_for(gsf_a, gsf_b, a_seg_rows, row) : alpha;
+      uint32_t y = f32_to_bf16(__fmul_rn(al, __fmul_rn(acc[e], kAccUnscale)));
+      if (bias != nullptr) y = add_bias_bf16(y, bias[col]);
+      out[row * n + col] = (uint16_t)y;
+    }
+  }
+}
+
+// K splits of gemm_decode_kernel: enough blocks for two per compute unit, each wave
+// keeping at least two super tiles.
+int decode_splits(int64_t k, int64_t n, int cus) {
+  const int64_t tiles = (n + kDecRows - 1) / kDecRows;
+  const int64_t st = ((k + BK - 1) / BK + 1) / 2;
+  int64_t sp = (2 * cus + tiles - 1) / tiles;
+  const int64_t max_sp = st / (2 * kWaves) > 0 ? st / (2 * kWaves) : 1;
   if (sp > max_sp) sp = max_sp;
   return (int)(sp < 1 ? 1 : sp);
 }
@@ -278,9 +418,12 @@ bool linear_skinny_fused_supported(int64_t m, int64_t k, int64_t n, const void* 
   const int sp = skinny_splits(k, n, cus);
   const int64_t range = (st_all + sp - 1) / sp;     // super tiles a block stages
   // staging costs about one 16-block per thread and row on the critical path: worth it
-  // while it stays within two per thread (measured: one row gains a launch, 16 rows lose)
+  // while it stays within two per thread (measured: one row gains a launch, 16 rows lose),
+  // and only for small weights: on larger ones the streaming of gemm_decode_kernel gains
+  // more than the launch (measured, one row: k_proj 8.3 vs 9.0 us, q_proj 13.3 vs 11.8 us)
   return m >= 1 && m <= 16 && k % 32 == 0 && (((uintptr_t)x | (uintptr_t)b_codes) & 15) == 0 &&
-         ((uintptr_t)b_scales & 3) == 0 && range <= kFusedMaxSt && m * range * 16 <= 2 * 256;
+         ((uintptr_t)b_scales & 3) == 0 && range <= kFusedMaxSt && m * range * 16 <= 2 * 256 &&
+         n * k <= ((int64_t)1 << 23);
 }
 
 hipError_t launch_linear_skinny_fused(const uint16_t* x, int64_t m, int64_t k, const uint8_t* b_codes,
@@ -308,7 +451,9 @@ bool gemm_skinny_supported(int64_t m, int64_t k, const void* a_codes, const void
 }
 
 size_t gemm_skinny_workspace_bytes(int64_t m, int64_t k, int64_t n, int cus) {
-  const int sp = skinny_splits(k, n, cus);
+  // m <= 16 also covers the static-scale fused launch, which splits like gemm_skinny_kernel
+  int64_t sp = skinny_splits(k, n, cus);
+  if (m <= 16) sp = std::max<int64_t>(sp, decode_splits(k, n, cus));
   return sp > 1 ? (size_t)sp * (size_t)m * (size_t)n * sizeof(float) : 0;
 }
 
@@ -316,15 +461,23 @@ hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales, i
                               const uint8_t* b_codes, const uint8_t* b_scales, int64_t n, const float* gsf_a,
                               const float* gsf_b, int64_t a_seg_rows, const uint16_t* bias, uint16_t* out,
                               void* workspace, size_t workspace_bytes, int cus, hipStream_t s) {
-  int splits = skinny_splits(k, n, cus);
+  int splits = m <= 16 ? decode_splits(k, n, cus) : skinny_splits(k, n, cus);
   const size_t need = splits > 1 ? (size_t)splits * (size_t)m * (size_t)n * sizeof(float) : 0;
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) splits = 1;
   float* partial = splits > 1 ? static_cast<float*>(workspace) : nullptr;
   hipError_t e;
-  if (m <= 16) e = launch_mt<1>(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, a_seg_rows, out, splits, partial, s);
-  else if (m <= 32) e = launch_mt<2>(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, a_seg_rows, out, splits, partial, s);
-  else if (m <= 64) e = launch_mt<4>(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, a_seg_rows, out, splits, partial, s);
-  else e = launch_mt<8>(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, a_seg_rows, out, splits, partial, s);
+  if (m <= 16) {
+    const int64_t tiles = (n + kDecRows - 1) / kDecRows;
+    hipLaunchKernelGGL(gemm_decode_kernel, dim3((uint32_t)(tiles * splits)), dim3(256), 0, s, a_codes, a_scales, m, k,
+                       b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, splits, partial);
+    e = hipGetLastError();
+  } else if (m <= 32) {
+    e = launch_mt<2>(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, a_seg_rows, out, splits, partial, s);
+  } else if (m <= 64) {
+    e = launch_mt<4>(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, a_seg_rows, out, splits, partial, s);
+  } else {
+    e = launch_mt<8>(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, a_seg_rows, out, splits, partial, s);
+  }
   if (e != hipSuccess || splits == 1) return e;
   const int64_t total = m * n;
   hipLaunchKernelGGL(gemm_skinny_reduce, dim3((uint32_t)((total + 255) / 256)), dim3(256), 0, s, partial, splits, m,
