@@ -103,14 +103,16 @@ __device__ __forceinline__ void interleave() {
 
 // kSplit: the launch for the tiles past the last whole round, each split along K into
 // fp32 partials (`splits` blocks per tile); otherwise whole tiles with the epilogue.
-// kTM: 32-row MFMA tiles per wave along M (4: 256 x 256 tiles, 2: 128 x 256).
+// kTM: 32-row MFMA tiles per wave along M (4: 256 x 256 tiles, 2: 128 x 256).  With
+// sub = 2 (split launch of 128-row tiles only), tile indices count tiles twice as tall
+// (tiles_m of that grid), each cut into two 128-row halves: tile tile0 + u / 2, half u % 2.
 template <bool kSplit, int kTM>
 __global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m, int64_t k,
     const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, int64_t n,
     const float* __restrict__ gsf_a, const float* __restrict__ gsf_b, int64_t a_seg_rows,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int64_t b_srows, int64_t ldo, int tiles_m,
-    int tiles_n, int tile0, int splits,
+    int tiles_n, int tile0, int splits, int sub,
     float* __restrict__ partial) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   using G = Geo<kTM>;
@@ -121,17 +123,19 @@ __global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
   // range b % splits of tile b / splits.
   const int nblk = gridDim.x;
   int bid = blockIdx.x;
-  int split = 0;
+  int split = 0, half = 0;
   if (kSplit) {
     split = bid % splits;
     bid = bid / splits;
+    half = bid % sub;
+    bid = bid / sub;
   } else if ((nblk & 7) == 0) {
     bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
   }
   bid += tile0;
   int tm, tn;
   tile_coords(bid, tiles_m, tiles_n, tm, tn);
-  const int64_t row0 = (int64_t)tm * G::kRowsA;
+  const int64_t row0 = ((int64_t)tm * sub + half) * G::kRowsA;
   const int64_t col0 = (int64_t)tn * kRows;
 
   const int t = threadIdx.x;
@@ -414,7 +418,7 @@ __global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
 // wave; consecutive threads take consecutive l, so the partial reads coalesce.
 template <int kTM>
 __global__ void __launch_bounds__(256) split_k_reduce(const float* __restrict__ partial, int splits, int tiles,
-                                                      int tile0, int tiles_m, int64_t m, int64_t n,
+                                                      int tile0, int sub, int tiles_m, int64_t m, int64_t n,
                                                       const float* __restrict__ gsf_a, const float* __restrict__ gsf_b,
                                                       int64_t a_seg_rows, const uint16_t* __restrict__ bias,
                                                       uint16_t* __restrict__ out, int64_t ldo) {
@@ -456,10 +460,10 @@ __global__ void __launch_bounds__(256) split_k_reduce(const float* __restrict__ 
 #pragma unroll
     for (int h = 0; h < 8; ++h) acc[h] += v[h];
   }
-  const int tile = tile0 + tl;
+  const int tile = tile0 + tl / sub;
   int tm, tn;
   tile_coords(tile, tiles_m, (int)((n + kRows - 1) / kRows), tm, tn);
-  const int64_t row = (int64_t)tm * G::kRowsA + (wave >> 1) * (32 * kTM) + i * 32 + l;
+  const int64_t row = ((int64_t)tm * sub + tl % sub) * G::kRowsA + (wave >> 1) * (32 * kTM) + i * 32 + l;
   const int64_t col = (int64_t)tn * kRows + (wave & 1) * 128 + j * 32 + 8 * qq;
   if (row >= m || col >= n) return;
   const float alpha = alpha_for(gsf_a, gsf_b, a_seg_rows, row);
@@ -490,7 +494,8 @@ struct PipePlan {
   int64_t tiles_m, tiles_n, full, rest;
   int splits;
   int tm;                  // kTM of the kernel
-  size_t partial_floats;   // per split tile
+  int sub;                 // 2: the split tail runs as 128-row halves (kTM 2) of the rest tiles
+  size_t partial_floats;   // per split unit (tile or half)
 };
 
 PipePlan pipe_plan(int64_t m, int64_t k, int64_t n, int cus) {
@@ -504,9 +509,21 @@ PipePlan pipe_plan(int64_t m, int64_t k, int64_t n, int cus) {
   p.full = tiles / cus * cus;
   p.rest = tiles - p.full;
   p.splits = 1;
+  p.sub = 1;
   const int64_t kt = (k + BK - 1) / BK;
   if (p.rest > 0) {
-    int64_t sp = cus / p.rest;              // at most one round: partials <= cus tiles
+    // With 256-row tiles and few of them left, their 128-row halves split half as many
+    // ways fill the GPU as well and write half the partials; worth it while K is short
+    // enough that the halves' lower MFMA rate costs less than the partials it saves
+    // (measured: K = 5120 gains 9 us, K = 8192 loses 2 us, K = 25600 loses 20 us).
+    const bool no_empty_half = m % 256 == 0 || m % 256 > 128;   // the last tile row's halves both hold rows
+    if (p.tm == 4 && kt <= 48 && no_empty_half && 2 * p.rest <= cus && kt >= 2 * (cus / (2 * p.rest)) &&
+        cus / (2 * p.rest) >= 2) {
+      p.sub = 2;
+      p.partial_floats = (size_t)128 * kRows;
+    }
+    const int64_t units = p.rest * p.sub;
+    int64_t sp = cus / units;               // at most one round: partials <= cus units
     while (sp > 1 && kt < 2 * sp) --sp;     // keep at least two K tiles per split
     p.splits = (int)(sp < 1 ? 1 : sp);
   }
@@ -514,7 +531,34 @@ PipePlan pipe_plan(int64_t m, int64_t k, int64_t n, int cus) {
 }
 
 size_t plan_bytes(const PipePlan& p) {
-  return p.splits > 1 ? (size_t)p.splits * (size_t)p.rest * p.partial_floats * sizeof(float) : 0;
+  return p.splits > 1 ? (size_t)p.splits * (size_t)(p.rest * p.sub) * p.partial_floats * sizeof(float) : 0;
+}
+
+// The K-split tail: `units` split tiles (or halves, sub = 2) from tile index tile0 of a
+// grid of tiles_m x tiles_n tiles, then the reduce.
+template <int kTM>
+hipError_t launch_split_tail(const PipePlan& p, int sub, const uint8_t* a_codes, const uint8_t* a_scales, int64_t m,
+                             int64_t k, const uint8_t* b_codes, const uint8_t* b_scales, int64_t n, const float* gsf_a,
+                             const float* gsf_b, int64_t a_seg_rows, const uint16_t* bias, uint16_t* out,
+                             float* partial, hipStream_t s) {
+  constexpr int kLds = Geo<kTM>::kLds;
+  static bool attr_set = false;
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_pipe_kernel<true, kTM>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int tm = (int)p.tiles_m, tn = (int)p.tiles_n;
+  const int64_t units = p.rest * sub;
+  hipLaunchKernelGGL((gemm_pipe_kernel<true, kTM>), dim3((uint32_t)(units * p.splits)), dim3(256), kLds, s, a_codes,
+                     a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, n, n, tm, tn,
+                     (int)p.full, p.splits, sub, partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((split_k_reduce<kTM>), dim3((uint32_t)(units * Geo<kTM>::kAcc / 8)), dim3(256), 0, s, partial,
+                     p.splits, (int)units, (int)p.full, sub, tm, m, n, gsf_a, gsf_b, a_seg_rows, bias, out, n);
+  return hipGetLastError();
 }
 
 template <int kTM>
@@ -525,18 +569,15 @@ hipError_t launch_plan(const PipePlan& p, const uint8_t* a_codes, const uint8_t*
   constexpr int kLds = Geo<kTM>::kLds;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_pipe_kernel<false, kTM>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_pipe_kernel<true, kTM>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_pipe_kernel<false, kTM>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int tm = (int)p.tiles_m, tn = (int)p.tiles_n;
   if (p.full > 0) {
     hipLaunchKernelGGL((gemm_pipe_kernel<false, kTM>), dim3((uint32_t)p.full), dim3(256), kLds, s, a_codes, a_scales,
-                       m, k, b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, n, n, tm, tn, 0, 1,
+                       m, k, b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, n, n, tm, tn, 0, 1, 1,
                        (float*)nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -545,17 +586,14 @@ hipError_t launch_plan(const PipePlan& p, const uint8_t* a_codes, const uint8_t*
   if (p.splits == 1) {
     hipLaunchKernelGGL((gemm_pipe_kernel<false, kTM>), dim3((uint32_t)p.rest), dim3(256), kLds, s, a_codes, a_scales,
                        m, k, b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, n, n, tm, tn, (int)p.full, 1,
-                       (float*)nullptr);
+                       1, (float*)nullptr);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((gemm_pipe_kernel<true, kTM>), dim3((uint32_t)(p.rest * p.splits)), dim3(256), kLds, s, a_codes,
-                     a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, n, n, tm, tn,
-                     (int)p.full, p.splits, partial);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((split_k_reduce<kTM>), dim3((uint32_t)(p.rest * Geo<kTM>::kAcc / 8)), dim3(256), 0, s, partial,
-                     p.splits, (int)p.rest, (int)p.full, tm, m, n, gsf_a, gsf_b, a_seg_rows, bias, out, n);
-  return hipGetLastError();
+  if (kTM == 4 && p.sub == 2)
+    return launch_split_tail<2>(p, 2, a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias,
+                                out, partial, s);
+  return launch_split_tail<kTM>(p, 1, a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias,
+                                out, partial, s);
 }
 
 }  // namespace

@@ -40,8 +40,11 @@ def test_sizes():
     assert L.nvfp4_quantize_workspace_bytes() % 256 == 0 and L.nvfp4_quantize_workspace_bytes() >= 4096
     ws = L.nvfp4_linear_workspace_bytes(4096, 5120, 1024)
     assert ws >= 4096 * 2560 + 40 * 4096 * 8 + 4096 + 4 and ws % 256 == 0
-    # 64 tiles of 256x256 on 256 CUs split four ways: 4 * 64 fp32 tiles of partials
-    assert L.nvfp4_gemm_workspace_bytes(4096, 5120, 1024) == 4 * 64 * 65536 * 4
+    # 64 tiles of 256x256 on 256 CUs, K = 5120: their 128 halves of 128x256 split two
+    # ways, 2 * 128 fp32 halves of partials
+    assert L.nvfp4_gemm_workspace_bytes(4096, 5120, 1024) == 2 * 128 * 32768 * 4
+    # ... and at K = 25600 the 256-row tiles split four ways
+    assert L.nvfp4_gemm_workspace_bytes(4096, 25600, 1024) == 4 * 64 * 65536 * 4
     assert L.nvfp4_gemm_workspace_bytes(4096, 5120, 16384) == 0      # whole rounds only
     # few rows: 16 column groups of 64, K split 5 ways (20 super tiles of 256, >= 4 per block)
     assert L.nvfp4_gemm_workspace_bytes(100, 5120, 1024) == 5 * 100 * 1024 * 4

@@ -68,10 +68,13 @@ def test_large_tile_path(m, n, k):
     assert_gemm_close(got[rows], ref, bound)
 
 
-@pytest.mark.parametrize("m,n,k", [(4096, 1024, 5120), (4096, 5120, 1024), (1000, 3000, 640)])
+@pytest.mark.parametrize("m,n,k", [(4096, 1024, 5120), (4096, 5120, 1024), (1000, 3000, 640), (4296, 1024, 5120),
+                                   (4096, 1024, 8192)])
 def test_split_k_tail(m, n, k):
     """Tiles past the last whole round are split along K into a workspace and summed in a
-    fixed order: same oracle tolerance, bitwise repeatable, and close to the unsplit run."""
+    fixed order: same oracle tolerance, bitwise repeatable, and close to the unsplit run.
+    Up to K = 6144 the 256-row tail tiles run as 128-row halves (a ragged last tile row
+    in the third and fourth cases); at K = 8192 as whole tiles."""
     rng = np.random.default_rng(m * 3 + n + k)
     px, sx = random_operands(rng, m, k)
     pw, sw = random_operands(rng, n, k)
