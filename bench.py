@@ -278,7 +278,7 @@ def main():
         "quantize_hbm_frac": round(q_gbs / PEAK_HBM_GBS, 4),
         "quantize_traffic": None if q_traffic is None else round(q_traffic),
         "roofline": {"kernel": "nvfp4_gemm: gemm_pipe_kernel<false, 4> (1536 whole 256x256 tiles) + "
-                               "gemm_pipe_kernel<true, 4> (64 tiles x 4 K splits) + split_k_reduce",
+                               "gemm_pipe_kernel<true, 2> (128 halves of 128x256 x 2 K splits) + split_k_reduce<2>",
                      "bound": "mfma",
                      "achieved": round(g_tflops, 2), "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(g_tflops / PEAK_F16_MFMA_TFLOPS, 4),
