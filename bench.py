@@ -178,7 +178,7 @@ def cpu_baseline(x_cpu, w_cpu, rows: int, repeats: int = 1) -> dict:
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
-GEMM_KERNELS = ("::gemm_pipe_kernel<", "::split_k_reduce(")
+GEMM_KERNELS = ("::gemm_pipe_kernel<", "::split_k_reduce<")
 QUANT_KERNELS = ("::amax_partial_kernel<", "::quantize_kernel<")
 
 
