@@ -262,33 +262,60 @@ int skinny_splits(int64_t k, int64_t n, int cus) {
 }
 
 // Decode (m <= 16): a block owns 16 weight rows (one MFMA column tile) and a K range
-// whose 256-wide super tiles its four waves split into four consecutive quarters.  The
-// weight is read in whole 128-byte lines: each load instruction covers 8 rows of one
-// super tile (lane l: row l / 8, 16-byte chunk l % 8), so at any time a block streams
-// four sequential runs through 16 consecutive rows.  The lines go through a per-wave
-// LDS buffer into the MFMA layout (lane (n, g): row n, bytes 32 g .. 32 g + 31 of the
-// super tile; chunk c of row r sits in slot c ^ ((r / 2) % 8), which keeps both the
-// writes and the reads free of bank conflicts).  kDecDepth super tiles per wave are in
-// flight in registers.  The waves' sums are added through LDS in wave order; with a
-// block-level K split, fp32 partials go to gemm_skinny_reduce.
+// whose 256-wide super tiles its four waves split into four consecutive quarters.  Each
+// wave streams its quarter through a ring of kDecDepth LDS slots with direct
+// global -> LDS loads (global_load_lds), one slot per super tile: the 16 weight rows and
+// the m (<= 16, clamped) activation rows as whole 128-byte lines (load instruction h
+// covers rows 8h .. 8h + 7, lane l: row 8h + l / 8, 16-byte position l % 8), and the
+// two K tiles' scale words of both operands.  Chunk c of row r sits at position
+// c ^ ((r / 2) % 8), which keeps the 16-byte MFMA-layout reads (lane (n, g): row n,
+// bytes 32 g .. 32 g + 31 of the super tile) free of bank conflicts.  The loop has no
+// lane-dependent branch and its only waits are the explicit ones on the direct loads,
+// so a super tile's loads stay in flight while the previous one is multiplied.  The
+// waves' sums are added through LDS in wave order; with a block-level K split, fp32
+// partials go to gemm_skinny_reduce.
 constexpr int kDecRows = 16;
-constexpr int kDecDepth = 4;
+constexpr int kDecDepth = 2;                  // LDS slots (super tiles in flight) per wave
+constexpr int kDecSlot = 2 * 2048 + 2 * 256;  // B lines, A lines, B scale words, A scale words
+constexpr int kDecLoads = 6;                  // direct-load instructions per super tile and wave
 
 __device__ __forceinline__ int dec_swz(int r) { return (r >> 1) & 7; }
+
+// One direct global -> LDS load per lane (16 or 4 bytes; lane l lands at dst + l * bytes;
+// dst is wave-uniform and goes to M0).  Written as inline asm so that the compiler does
+// not track these loads: it would otherwise make every LDS read of the ring wait for all
+// of them (it cannot tell the slots apart across loop iterations).  The kernel waits for
+// them itself (dec_wait_*), and nothing else in it uses M0.
+__device__ __forceinline__ void dec_dma16(const uint8_t* src, uint8_t* dst) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"((uint32_t)(uintptr_t)dst), "v"(src) : "memory");
+}
+__device__ __forceinline__ void dec_dma4(const uint8_t* src, uint8_t* dst) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
+               :: "s"((uint32_t)(uintptr_t)dst), "v"(src) : "memory");
+}
+// Waits until at most one super tile's direct loads (the newer one) are in flight; the
+// compiler moves no memory access across it.
+__device__ __forceinline__ void dec_wait_one_behind() {
+  static_assert(kDecLoads == 6 && kDecDepth == 2, "wait count");
+  asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+}
+__device__ __forceinline__ void dec_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void dec_lds_order() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 __global__ void __launch_bounds__(256) gemm_decode_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m, int64_t k,
     const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, int64_t n,
     const float* __restrict__ gsf_a, const float* __restrict__ gsf_b, int64_t a_seg_rows,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int splits, float* __restrict__ partial) {
-  __shared__ __attribute__((aligned(16))) uint8_t buf[kWaves][kDecRows * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][kDecDepth][kDecSlot];
   __shared__ float red[kWaves - 1][4][64];
 
   const int tile = blockIdx.x / splits;
   const int split = blockIdx.x % splits;
   const int64_t n0 = (int64_t)tile * kDecRows;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: K range, LDS slots
   const int l16 = lane & 15;
   const int g = lane >> 4;
   const int64_t half_k = k / 2;
@@ -298,63 +325,83 @@ __global__ void __launch_bounds__(256) gemm_decode_kernel(
   const int64_t s0 = b0 + (b1 - b0) * wave / kWaves, s1 = b0 + (b1 - b0) * (wave + 1) / kWaves;
   const int count = (int)(s1 - s0);
 
-  // line loads: rows lr and lr + 8 of the tile, logical chunk lc (lands in slot lane % 8)
-  const int lr = lane >> 3;
-  const int lc0 = (lane & 7) ^ dec_swz(lr), lc1 = (lane & 7) ^ dec_swz(lr + 8);
+  // Direct-load sources.  Lines: lane l -> row lr (+ 8 for the second instruction) at
+  // position p, i.e. logical chunk p ^ dec_swz(row).  Scale words: lane l -> word l % 2
+  // of row (l % 32) / 2 in K tile 2 st + l / 32 (128 bytes per operand and K tile).
+  const int lr = lane >> 3, p = lane & 7;
+  const int lc0 = p ^ dec_swz(lr), lc1 = p ^ dec_swz(lr + 8);
   const uint8_t* bl0 = b_codes + min(n0 + lr, n - 1) * half_k + 16 * lc0;
   const uint8_t* bl1 = b_codes + min(n0 + lr + 8, n - 1) * half_k + 16 * lc1;
-  const int64_t nb = min(n0 + l16, n - 1);                    // this lane's MFMA column
-  const uint8_t* bs_row = b_scales + nb * 8 + 4 * (g & 1);
-  const int64_t ra = min((int64_t)l16, m - 1);                 // this lane's MFMA row of A
-  const uint8_t* a_row = a_codes + ra * half_k + 32 * g;
-  const uint8_t* as_row = a_scales + ra * 8 + 4 * (g & 1);
+  const uint8_t* al0 = a_codes + min((int64_t)lr, m - 1) * half_k + 16 * lc0;
+  const uint8_t* al1 = a_codes + min((int64_t)lr + 8, m - 1) * half_k + 16 * lc1;
+  const int sr = (lane & 31) >> 1, sh = lane >> 5;
+  const uint8_t* bsl = b_scales + min(n0 + sr, n - 1) * 8 + 4 * (lane & 1);
+  const uint8_t* asl = a_scales + min((int64_t)sr, m - 1) * 8 + 4 * (lane & 1);
 
-  struct Item {
-    uint4 b0, b1;       // two line chunks of the weight
-    uint4 a0, a1;       // this lane's 32 code bytes of A
-    uint32_t bs, as;    // the scale bytes of this lane's four 16-blocks
-  };
-  auto fetch = [&](int64_t st, Item& it) {
+  // Loads super tile st into a slot.  Super tiles past the wave's range re-load the last
+  // one (the slot is never multiplied); chunks past the end of a row (partial last super
+  // tile) re-load the row's first chunk, whose block scales there are the zero padding
+  // of the scale layout; the K tile past an odd count of K tiles re-loads the last one's
+  // scale words, and the lanes that own it use zero scales instead (multiply).
+  auto issue = [&](int64_t st, uint8_t* slot) {
+    st = min(st, st_all - 1);
     const int64_t off = st * 128;
-    const int64_t kt = 2 * st + (g >> 1);
-    const bool v0 = off + 16 * lc0 < half_k, v1 = off + 16 * lc1 < half_k;   // partial last super tile
-    it.b0 = v0 ? *reinterpret_cast<const uint4*>(bl0 + off) : make_uint4(0, 0, 0, 0);
-    it.b1 = v1 ? *reinterpret_cast<const uint4*>(bl1 + off) : make_uint4(0, 0, 0, 0);
-    const int64_t ao = off + 32 * g;
-    const bool c0 = ao < half_k, c1 = ao + 16 < half_k, sv = kt < kt_all;
-    it.a0 = c0 ? *reinterpret_cast<const uint4*>(a_row + off) : make_uint4(0, 0, 0, 0);
-    it.a1 = c1 ? *reinterpret_cast<const uint4*>(a_row + off + 16) : make_uint4(0, 0, 0, 0);
-    it.bs = sv ? *reinterpret_cast<const uint32_t*>(bs_row + kt * n * 8) : 0u;
-    it.as = sv ? *reinterpret_cast<const uint32_t*>(as_row + kt * m * 8) : 0u;
+    const int64_t o0 = off + 16 * lc0 < half_k ? off : -16 * lc0;
+    const int64_t o1 = off + 16 * lc1 < half_k ? off : -16 * lc1;
+    dec_dma16(bl0 + o0, slot);
+    dec_dma16(bl1 + o1, slot + 1024);
+    dec_dma16(al0 + o0, slot + 2048);
+    dec_dma16(al1 + o1, slot + 3072);
+    const int64_t kt = min(2 * st + sh, kt_all - 1);
+    dec_dma4(bsl + kt * n * 8, slot + 4096);
+    dec_dma4(asl + kt * m * 8, slot + 4096 + 256);
   };
+
   float4_t acc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  uint8_t* wb = buf[wave];
-  auto process = [&](const Item& it) {
-    // the wave's 16 rows x 128 bytes into LDS, then this lane's 32 bytes of row l16 back
-    *reinterpret_cast<uint4*>(wb + 16 * lane) = it.b0;
-    *reinterpret_cast<uint4*>(wb + 1024 + 16 * lane) = it.b1;
-    const uint4 w0 = *reinterpret_cast<const uint4*>(wb + l16 * 128 + 16 * ((2 * g) ^ dec_swz(l16)));
-    const uint4 w1 = *reinterpret_cast<const uint4*>(wb + l16 * 128 + 16 * ((2 * g + 1) ^ dec_swz(l16)));
+  // Multiplies the super tile st held in a slot: lane (l16, g) takes bytes 32 g .. +31 of
+  // weight row l16 and activation row l16, and the scale word of K tile 2 st + g / 2.
+  auto multiply = [&](const uint8_t* slot, int64_t st) {
+    const int p0 = (2 * g) ^ dec_swz(l16), p1 = (2 * g + 1) ^ dec_swz(l16);
+    const uint4 w0 = *reinterpret_cast<const uint4*>(slot + l16 * 128 + 16 * p0);
+    const uint4 w1 = *reinterpret_cast<const uint4*>(slot + l16 * 128 + 16 * p1);
+    const uint4 x0 = *reinterpret_cast<const uint4*>(slot + 2048 + l16 * 128 + 16 * p0);
+    const uint4 x1 = *reinterpret_cast<const uint4*>(slot + 2048 + l16 * 128 + 16 * p1);
+    const int so = (g >> 1) * 128 + l16 * 8 + 4 * (g & 1);
+    const uint32_t keep = 2 * st + (g >> 1) < kt_all ? ~0u : 0u;   // K tile exists
+    const uint32_t bs = *reinterpret_cast<const uint32_t*>(slot + 4096 + so) & keep;
+    const uint32_t as = *reinterpret_cast<const uint32_t*>(slot + 4096 + 256 + so) & keep;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {                     // K values [64g + 8s, +8): block s/2
-      const half8_t fb = dequant8(word(s < 4 ? w0 : w1, s & 3), scale_pair(it.bs, s >> 1));
-      const half8_t fa = dequant8(word(s < 4 ? it.a0 : it.a1, s & 3), scale_pair(it.as, s >> 1));
+      const half8_t fb = dequant8(word(s < 4 ? w0 : w1, s & 3), scale_pair(bs, s >> 1));
+      const half8_t fa = dequant8(word(s < 4 ? x0 : x1, s & 3), scale_pair(as, s >> 1));
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fb, acc, 0, 0, 0);
     }
   };
-  Item ring[kDecDepth];
-#pragma unroll
-  for (int u = 0; u < kDecDepth; ++u)
-    if (u < count) fetch(s0 + u, ring[u]);
-  for (int t = 0; t < count; t += kDecDepth) {
-#pragma unroll
-    for (int u = 0; u < kDecDepth; ++u) {
-      if (t + u < count) {
-        process(ring[u]);
-        if (t + u + kDecDepth < count) fetch(s0 + t + u + kDecDepth, ring[u]);
-      }
-    }
+
+  // Super tiles s0 + i and s0 + i + 1 from slots sa and sb.  The two slots are distinct
+  // and the restrict qualifiers tell the compiler so: reading one slot then does not
+  // wait for the direct loads still filling the other.
+  // The loop body has no branch (a merge point would make the compiler's wait tracking
+  // forget which slot a load fills); an odd last super tile is multiplied after it.
+  auto pair = [&](uint8_t* __restrict__ sa, uint8_t* __restrict__ sb, int i) __attribute__((always_inline)) {
+    dec_wait_one_behind();          // super tile s0 + i has landed
+    multiply(sa, s0 + i);
+    dec_lds_order();                // its reads are done before the slot is refilled
+    issue(s0 + i + 2, sa);
+    dec_wait_one_behind();
+    multiply(sb, s0 + i + 1);
+    dec_lds_order();
+    issue(s0 + i + 3, sb);
+  };
+  issue(s0, ring[wave][0]);
+  issue(s0 + 1, ring[wave][1]);
+  int i = 0;
+  for (; i + 1 < count; i += 2) pair(ring[wave][0], ring[wave][1], i);
+  if (i < count) {
+    dec_wait_one_behind();
+    multiply(ring[wave][0], s0 + i);
   }
+  dec_wait_all();                   // nothing still landing in this wave's slots
 
   // Sum the four waves' K quarters in wave order: ((w0 + w1) + w2) + w3.
   if (wave > 0) {
