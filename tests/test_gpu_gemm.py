@@ -188,10 +188,10 @@ def test_probe_near_the_pages_figure():
 
 
 @pytest.mark.parametrize("m", [1, 5, 16, 17, 40, 64, 100, 128])
-@pytest.mark.parametrize("n,k", [(1024, 5120), (300, 4128), (5120, 1024)])
+@pytest.mark.parametrize("n,k", [(1024, 5120), (300, 4128), (5120, 1024), (301, 1056)])
 def test_few_rows_weight_streaming(m, n, k):
     """Decode shapes (M <= 128): the weight-streaming kernel, with and without the
-    block-level K split, against the oracle; ragged N and a partial last K tile."""
+    block-level K split, against the oracle; ragged and odd N and a partial last K tile."""
     rng = np.random.default_rng(m * 7 + n + k)
     px, sx = random_operands(rng, m, k)
     pw, sw = random_operands(rng, n, k)
