@@ -73,9 +73,10 @@ size_t nvfp4_scale_bytes(int64_t rows, int64_t k);
 size_t nvfp4_quantize_workspace_bytes(void);
 
 /* Workspace nvfp4_linear needs for an [m, k] input and n outputs: activation codes
- * [m][k/2], their scales, amax partials, the activation global scale and the GEMM's
- * split-K partial sums (nvfp4_gemm_workspace_bytes), each 256-byte aligned.  Depends on
- * the compute-unit count of the current device. */
+ * [m][k/2], their scales, amax partials, the activation global scale, the GEMM's
+ * split-K partial sums (nvfp4_gemm_workspace_bytes) and, for m <= 4, the quantized
+ * activation in fp16 [m][k] (the decode GEMM then expands only the weight), each
+ * 256-byte aligned.  Depends on the compute-unit count of the current device. */
 size_t nvfp4_linear_workspace_bytes(int64_t m, int64_t k, int64_t n);
 
 /* Workspace nvfp4_linear_segmented needs for `segments` row blocks of seg_rows rows:

@@ -66,12 +66,14 @@ struct LinearWorkspace {
   float* partials;
   float* gsf;
   void* gemm;
+  uint16_t* a16;   // the activation's fp16 operand form (m <= kDecodeA16Rows), or NULL
   size_t gemm_bytes;
   size_t bytes;
 };
 
 // Layout of an nvfp4_linear workspace: codes, scales, amax partials, one global scale
-// per segment, then the GEMM's split-K partials; every piece 256-byte aligned.
+// per segment, the GEMM's split-K partials, then (m <= kDecodeA16Rows) the fp16 operand
+// form of the activation for the decode GEMM; every piece 256-byte aligned.
 LinearWorkspace carve(void* base, int64_t m, int64_t k, int64_t n, int64_t segments = 1) {
   // offsets first, pointers only for a real base
   const size_t o_codes = 0;
@@ -80,7 +82,9 @@ LinearWorkspace carve(void* base, int64_t m, int64_t k, int64_t n, int64_t segme
   const size_t o_gsf = align_up(o_partials + sizeof(float) * nvfp4::kMaxAmaxPartials);
   const size_t o_gemm = align_up(o_gsf + sizeof(float) * (size_t)segments);
   const size_t gemm_bytes = nvfp4::gemm_workspace_bytes(m, k, n);
-  LinearWorkspace w{nullptr, nullptr, nullptr, nullptr, nullptr, gemm_bytes, align_up(o_gemm + gemm_bytes)};
+  const size_t o_a16 = align_up(o_gemm + gemm_bytes);
+  const size_t a16_bytes = m <= nvfp4::kDecodeA16Rows && segments == 1 ? (size_t)m * (size_t)k * 2u : 0;
+  LinearWorkspace w{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, gemm_bytes, align_up(o_a16 + a16_bytes)};
   if (base != nullptr) {
     uint8_t* p = static_cast<uint8_t*>(base);
     w.codes = p + o_codes;
@@ -88,6 +92,7 @@ LinearWorkspace carve(void* base, int64_t m, int64_t k, int64_t n, int64_t segme
     w.partials = reinterpret_cast<float*>(p + o_partials);
     w.gsf = reinterpret_cast<float*>(p + o_gsf);
     w.gemm = gemm_bytes ? p + o_gemm : nullptr;
+    w.a16 = a16_bytes ? reinterpret_cast<uint16_t*>(p + o_a16) : nullptr;
   }
   return w;
 }
@@ -99,7 +104,7 @@ LinearWorkspace carve(void* base, int64_t m, int64_t k, int64_t n, int64_t segme
 // amax pass, which stores it in xbuf ([m][k] bf16) for the quantize pass to read.
 int quantize_impl(const char* fn, const void* x, int64_t m, int64_t k, const float* gsf_static, int group,
                   uint8_t* codes, uint8_t* scales, float* gsf_out, float* partials, hipStream_t s,
-                  int64_t segments = 1, const void* up = nullptr, void* xbuf = nullptr) {
+                  int64_t segments = 1, const void* up = nullptr, void* xbuf = nullptr, uint16_t* a16 = nullptr) {
   int n_partials = 0;
   const float c = inv_sqrt(group);
   const int64_t seg_rows = m / segments;
@@ -116,7 +121,7 @@ int quantize_impl(const char* fn, const void* x, int64_t m, int64_t k, const flo
     }
   }
   return hip_status(nvfp4::launch_quantize(xp, upp, m, k, group, c, gsf_static, partials, n_partials, seg_rows,
-                                           (int)segments, codes, scales, gsf_out, s), fn);
+                                           (int)segments, codes, scales, gsf_out, s, a16), fn);
 }
 
 size_t product_bytes(int64_t m, int64_t k) { return align_up((size_t)m * (size_t)k * 2u); }
@@ -166,9 +171,18 @@ int linear_impl(const char* fn, const void* x, int64_t segments, int64_t seg_row
   float* gsf = gsf_out != nullptr ? gsf_out : ws.gsf;   // the GEMM reads the scales where they were written
   const bool per_segment = global_sf_x == nullptr && segments > 1;
   void* xbuf = keep_product ? static_cast<uint8_t*>(workspace) + base : nullptr;
+  // a few rows: the quantize pass also writes the fp16 operand form, and the decode GEMM
+  // then expands only the weight
+  const bool a16 = ws.a16 != nullptr && !per_segment &&
+                   nvfp4::gemm_decode_a16_supported(m, k, ws.a16, packed, inv_scale);
   if (int rc = quantize_impl(fn, x, m, k, global_sf_x, rotation_group, ws.codes, ws.scales, gsf, ws.partials, s,
-                             per_segment ? segments : 1, up, xbuf))
+                             per_segment ? segments : 1, up, xbuf, a16 ? ws.a16 : nullptr))
     return rc;
+  if (a16)
+    return hip_status(nvfp4::launch_gemm_decode_a16(ws.a16, m, k, packed, inv_scale, out_features, gsf, global_sf_w,
+                                                    static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(out),
+                                                    ws.gemm, ws.gemm_bytes, nvfp4::compute_units(), s),
+                      fn);
   return hip_status(nvfp4::launch_gemm(ws.codes, ws.scales, m, k, packed, inv_scale, out_features, gsf, global_sf_w,
                                        per_segment ? seg_rows : 0, static_cast<const uint16_t*>(bias),
                                        static_cast<uint16_t*>(out), ws.gemm, ws.gemm_bytes, s),

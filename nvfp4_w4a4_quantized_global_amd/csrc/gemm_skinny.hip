@@ -277,7 +277,6 @@ int skinny_splits(int64_t k, int64_t n, int cus) {
 constexpr int kDecRows = 16;
 constexpr int kDecDepth = 2;                  // LDS slots (super tiles in flight) per wave
 constexpr int kDecSlot = 2 * 2048 + 2 * 256;  // B lines, A lines, B scale words, A scale words
-constexpr int kDecLoads = 6;                  // direct-load instructions per super tile and wave
 
 __device__ __forceinline__ int dec_swz(int r) { return (r >> 1) & 7; }
 
@@ -294,20 +293,31 @@ __device__ __forceinline__ void dec_dma4(const uint8_t* src, uint8_t* dst) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
                :: "s"((uint32_t)(uintptr_t)dst), "v"(src) : "memory");
 }
-// Waits until at most one super tile's direct loads (the newer one) are in flight; the
-// compiler moves no memory access across it.
+// Waits until at most one super tile's kLoads direct loads (the newer one) are in
+// flight; the compiler moves no memory access across it.
+template <int kLoads>
 __device__ __forceinline__ void dec_wait_one_behind() {
-  static_assert(kDecLoads == 6 && kDecDepth == 2, "wait count");
-  asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  static_assert(kDecDepth == 2 && (kLoads == 5 || kLoads == 6), "wait count");
+  if constexpr (kLoads == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
 }
 __device__ __forceinline__ void dec_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void dec_lds_order() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// kA16: the activation arrives as its fp16 operand form a16 [m][k] (m <= 4) instead of
+// codes and scales.  A slot then holds rows 0 .. 3 (clamped to m - 1) of a16 for the
+// super tile, 512 bytes each, 16-byte chunk c of row r at position c ^ r (the 16 lanes
+// that read one chunk of rows l16 % 4 hit four distinct bank groups), and the kernel
+// expands only the weight.  MFMA rows 4 .. 15 multiply rows l16 % 4 again, into output
+// rows that are never written.
+template <bool kA16>
 __global__ void __launch_bounds__(256) gemm_decode_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m, int64_t k,
     const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, int64_t n,
     const float* __restrict__ gsf_a, const float* __restrict__ gsf_b, int64_t a_seg_rows,
-    const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int splits, float* __restrict__ partial) {
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int splits, float* __restrict__ partial,
+    const uint16_t* __restrict__ a16) {
+  constexpr int kLoads = kA16 ? 5 : 6;   // direct-load instructions per super tile and wave
   __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][kDecDepth][kDecSlot];
   __shared__ float red[kWaves - 1][4][64];
 
@@ -336,7 +346,13 @@ __global__ void __launch_bounds__(256) gemm_decode_kernel(
   const uint8_t* al1 = a_codes + min((int64_t)lr + 8, m - 1) * half_k + 16 * lc1;
   const int sr = (lane & 31) >> 1, sh = lane >> 5;
   const uint8_t* bsl = b_scales + min(n0 + sr, n - 1) * 8 + 4 * (lane & 1);
-  const uint8_t* asl = a_scales + min((int64_t)sr, m - 1) * 8 + 4 * (lane & 1);
+  const uint8_t* asl = kA16 ? nullptr : a_scales + min((int64_t)sr, m - 1) * 8 + 4 * (lane & 1);
+  // a16 lines: instruction h, lane l -> row 2 h + l / 32, position l % 32, logical chunk
+  // (l % 32) ^ row of the super tile's 256 values
+  const int ar0 = lane >> 5, ar1 = 2 + (lane >> 5), ap = lane & 31;
+  const int ac0 = ap ^ ar0, ac1 = ap ^ ar1;
+  const uint16_t* xl0 = kA16 ? a16 + min((int64_t)ar0, m - 1) * k + 8 * ac0 : nullptr;
+  const uint16_t* xl1 = kA16 ? a16 + min((int64_t)ar1, m - 1) * k + 8 * ac1 : nullptr;
 
   // Loads super tile st into a slot.  Super tiles past the wave's range re-load the last
   // one (the slot is never multiplied); chunks past the end of a row (partial last super
@@ -350,11 +366,18 @@ __global__ void __launch_bounds__(256) gemm_decode_kernel(
     const int64_t o1 = off + 16 * lc1 < half_k ? off : -16 * lc1;
     dec_dma16(bl0 + o0, slot);
     dec_dma16(bl1 + o1, slot + 1024);
-    dec_dma16(al0 + o0, slot + 2048);
-    dec_dma16(al1 + o1, slot + 3072);
+    if (kA16) {
+      // values past the end of a row re-load the row's first chunk (zero weight scales)
+      const int64_t e = st * 256;
+      dec_dma16(reinterpret_cast<const uint8_t*>(xl0 + (e + 8 * ac0 < k ? e : -8 * ac0)), slot + 2048);
+      dec_dma16(reinterpret_cast<const uint8_t*>(xl1 + (e + 8 * ac1 < k ? e : -8 * ac1)), slot + 3072);
+    } else {
+      dec_dma16(al0 + o0, slot + 2048);
+      dec_dma16(al1 + o1, slot + 3072);
+    }
     const int64_t kt = min(2 * st + sh, kt_all - 1);
     dec_dma4(bsl + kt * n * 8, slot + 4096);
-    dec_dma4(asl + kt * m * 8, slot + 4096 + 256);
+    if (!kA16) dec_dma4(asl + kt * m * 8, slot + 4096 + 256);
   };
 
   float4_t acc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -369,11 +392,14 @@ __global__ void __launch_bounds__(256) gemm_decode_kernel(
     const int so = (g >> 1) * 128 + l16 * 8 + 4 * (g & 1);
     const uint32_t keep = 2 * st + (g >> 1) < kt_all ? ~0u : 0u;   // K tile exists
     const uint32_t bs = *reinterpret_cast<const uint32_t*>(slot + 4096 + so) & keep;
-    const uint32_t as = *reinterpret_cast<const uint32_t*>(slot + 4096 + 256 + so) & keep;
+    const uint32_t as = kA16 ? 0u : *reinterpret_cast<const uint32_t*>(slot + 4096 + 256 + so) & keep;
+    const int xr = l16 & 3;   // kA16: the a16 row this lane reads
 #pragma unroll
     for (int s = 0; s < 8; ++s) {                     // K values [64g + 8s, +8): block s/2
       const half8_t fb = dequant8(word(s < 4 ? w0 : w1, s & 3), scale_pair(bs, s >> 1));
-      const half8_t fa = dequant8(word(s < 4 ? x0 : x1, s & 3), scale_pair(as, s >> 1));
+      const half8_t fa =
+          kA16 ? *reinterpret_cast<const half8_t*>(slot + 2048 + xr * 512 + 16 * ((8 * g + s) ^ xr))
+               : dequant8(word(s < 4 ? x0 : x1, s & 3), scale_pair(as, s >> 1));
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fb, acc, 0, 0, 0);
     }
   };
@@ -384,11 +410,11 @@ __global__ void __launch_bounds__(256) gemm_decode_kernel(
   // The loop body has no branch (a merge point would make the compiler's wait tracking
   // forget which slot a load fills); an odd last super tile is multiplied after it.
   auto pair = [&](uint8_t* __restrict__ sa, uint8_t* __restrict__ sb, int i) __attribute__((always_inline)) {
-    dec_wait_one_behind();          // super tile s0 + i has landed
+    dec_wait_one_behind<kLoads>();          // super tile s0 + i has landed
     multiply(sa, s0 + i);
     dec_lds_order();                // its reads are done before the slot is refilled
     issue(s0 + i + 2, sa);
-    dec_wait_one_behind();
+    dec_wait_one_behind<kLoads>();
     multiply(sb, s0 + i + 1);
     dec_lds_order();
     issue(s0 + i + 3, sb);
@@ -398,7 +424,7 @@ __global__ void __launch_bounds__(256) gemm_decode_kernel(
   int i = 0;
   for (; i + 1 < count; i += 2) pair(ring[wave][0], ring[wave][1], i);
   if (i < count) {
-    dec_wait_one_behind();
+    dec_wait_one_behind<kLoads>();
     multiply(ring[wave][0], s0 + i);
   }
   dec_wait_all();                   // nothing still landing in this wave's slots
@@ -515,8 +541,9 @@ hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales, i
   hipError_t e;
   if (m <= 16) {
     const int64_t tiles = (n + kDecRows - 1) / kDecRows;
-    hipLaunchKernelGGL(gemm_decode_kernel, dim3((uint32_t)(tiles * splits)), dim3(256), 0, s, a_codes, a_scales, m, k,
-                       b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, splits, partial);
+    hipLaunchKernelGGL(gemm_decode_kernel<false>, dim3((uint32_t)(tiles * splits)), dim3(256), 0, s, a_codes,
+                       a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, splits, partial,
+                       (const uint16_t*)nullptr);
     e = hipGetLastError();
   } else if (m <= 32) {
     e = launch_mt<2>(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, a_seg_rows, out, splits, partial, s);
@@ -529,6 +556,31 @@ hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales, i
   const int64_t total = m * n;
   hipLaunchKernelGGL(gemm_skinny_reduce, dim3((uint32_t)((total + 255) / 256)), dim3(256), 0, s, partial, splits, m,
                      n, gsf_a, gsf_b, a_seg_rows, bias, out);
+  return hipGetLastError();
+}
+
+bool gemm_decode_a16_supported(int64_t m, int64_t k, const void* a16, const void* b_codes, const void* b_scales) {
+  return m >= 1 && m <= kDecodeA16Rows && k % 32 == 0 && (((uintptr_t)a16 | (uintptr_t)b_codes) & 15) == 0 &&
+         ((uintptr_t)b_scales & 3) == 0;
+}
+
+hipError_t launch_gemm_decode_a16(const uint16_t* a16, int64_t m, int64_t k, const uint8_t* b_codes,
+                                  const uint8_t* b_scales, int64_t n, const float* gsf_a, const float* gsf_b,
+                                  const uint16_t* bias, uint16_t* out, void* workspace, size_t workspace_bytes,
+                                  int cus, hipStream_t s) {
+  int splits = decode_splits(k, n, cus);
+  const size_t need = splits > 1 ? (size_t)splits * (size_t)m * (size_t)n * sizeof(float) : 0;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) splits = 1;
+  float* partial = splits > 1 ? static_cast<float*>(workspace) : nullptr;
+  const int64_t tiles = (n + kDecRows - 1) / kDecRows;
+  hipLaunchKernelGGL(gemm_decode_kernel<true>, dim3((uint32_t)(tiles * splits)), dim3(256), 0, s,
+                     (const uint8_t*)nullptr, (const uint8_t*)nullptr, m, k, b_codes, b_scales, n, gsf_a, gsf_b,
+                     (int64_t)0, bias, out, splits, partial, a16);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  const int64_t total = m * n;
+  hipLaunchKernelGGL(gemm_skinny_reduce, dim3((uint32_t)((total + 255) / 256)), dim3(256), 0, s, partial, splits, m,
+                     n, gsf_a, gsf_b, (int64_t)0, bias, out);
   return hipGetLastError();
 }
 

@@ -23,11 +23,13 @@ hipError_t launch_amax_partials(const uint16_t* x, const uint16_t* up, uint16_t*
 
 // Quantizes rows x [rows][k]; with static_gsf NULL, segment s (rows [s*seg_rows,
 // (s+1)*seg_rows)) takes its global scale from its n_partials partial maxima and
-// gsf_out[s] receives it.
+// gsf_out[s] receives it.  With a16 not NULL, a16 [rows][k] also receives every
+// quantized value as the exact fp16 code * scale * 2^-8 (the operand form of the GEMMs,
+// for gemm_decode_a16).
 hipError_t launch_quantize(const uint16_t* x, const uint16_t* up, int64_t rows, int64_t k, int group,
                            float inv_sqrt_g, const float* static_gsf, const float* partials, int n_partials,
                            int64_t seg_rows, int segments, uint8_t* codes, uint8_t* scales, float* gsf_out,
-                           hipStream_t s);
+                           hipStream_t s, uint16_t* a16 = nullptr);
 
 // x [rows][k] = bf16 SwiGLU product of gate and up.
 hipError_t launch_swiglu(const uint16_t* gate, const uint16_t* up, uint16_t* x, int64_t rows, int64_t k, hipStream_t s);
@@ -70,6 +72,17 @@ hipError_t launch_gemm_pipe(const uint8_t* a_codes, const uint8_t* a_scales, int
                             const uint8_t* b_codes, const uint8_t* b_scales, int64_t n, const float* gsf_a,
                             const float* gsf_b, int64_t a_seg_rows, const uint16_t* bias, uint16_t* out,
                             void* workspace, size_t workspace_bytes, int cus, hipStream_t s);
+
+// The decode GEMM for m <= kDecodeA16Rows activation rows given as the fp16 operand
+// form a16 [m][k] (launch_quantize's a16 output) instead of codes and scales, so the
+// kernel expands only the weight.  One activation scale (gsf_a[0]).  K a multiple of
+// 32, b_codes 16-byte and b_scales 4-byte aligned, a16 16-byte aligned.
+constexpr int kDecodeA16Rows = 4;
+bool gemm_decode_a16_supported(int64_t m, int64_t k, const void* a16, const void* b_codes, const void* b_scales);
+hipError_t launch_gemm_decode_a16(const uint16_t* a16, int64_t m, int64_t k, const uint8_t* b_codes,
+                                  const uint8_t* b_scales, int64_t n, const float* gsf_a, const float* gsf_b,
+                                  const uint16_t* bias, uint16_t* out, void* workspace, size_t workspace_bytes,
+                                  int cus, hipStream_t s);
 
 // The weight-streaming GEMM for m <= 128 (gemm_skinny.hip): K a multiple of 32, code
 // pointers 16-byte and scale pointers 4-byte aligned.  Splits K across blocks when the

@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gemm_common.h"
 #include "nvfp4_device.h"
 #include "nvfp4_launch.h"
 
@@ -143,7 +144,8 @@ __global__ void __launch_bounds__(kThreads) quantize_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ up, int64_t m_rows, int64_t k, int group,
     float inv_sqrt_g,
     const float* __restrict__ static_gsf, const float* __restrict__ partials, int n_partials, int64_t seg_rows,
-    int segments, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gsf_out) {
+    int segments, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gsf_out,
+    uint16_t* __restrict__ a16) {
   __shared__ uint32_t seg_amax[kMaxSegments];   // segment maxima, then global scales (bits)
   __shared__ float lds[kThreads / 64];
   const int64_t kt_count = (k + kScaleTileK - 1) / kScaleTileK;
@@ -206,6 +208,13 @@ __global__ void __launch_bounds__(kThreads) quantize_kernel(
       uint32_t w0, w1;
       const uint32_t s8 = quantize_block16(v[u], gsf, valid, w0, w1);
       if (valid) *reinterpret_cast<uint2*>(codes + row[u] * (k / 2) + blk * 8) = make_uint2(w0, w1);
+      if (a16 != nullptr && valid) {
+        // the block's values in the GEMMs' operand form: fp16 code * scale * 2^-8, exact
+        const gemm::half2_t sc = gemm::as_half2((s8 << 7) | (s8 << 23));
+        uint4* d = reinterpret_cast<uint4*>(a16 + row[u] * k + blk * kBlock);
+        d[0] = __builtin_bit_cast(uint4, gemm::dequant8(w0, sc));
+        d[1] = __builtin_bit_cast(uint4, gemm::dequant8(w1, sc));
+      }
       // gather the unit's 8 scale bytes into lane j == 0 and write them as one 8-byte word
       uint32_t lo = j < 4 ? s8 << (8 * j) : 0u;
       uint32_t hi = j >= 4 ? s8 << (8 * (j - 4)) : 0u;
@@ -361,7 +370,7 @@ hipError_t launch_amax_partials(const uint16_t* x, const uint16_t* up, uint16_t*
 hipError_t launch_quantize(const uint16_t* x, const uint16_t* up, int64_t rows, int64_t k, int group,
                            float inv_sqrt_g, const float* static_gsf, const float* partials, int n_partials,
                            int64_t seg_rows, int segments, uint8_t* codes, uint8_t* scales, float* gsf_out,
-                           hipStream_t s) {
+                           hipStream_t s, uint16_t* a16) {
   const int64_t kt_count = (k + kScaleTileK - 1) / kScaleTileK;
   const int64_t units = rows * kt_count;
   const int64_t per_block = (int64_t)kQuantUnits * (kThreads / 8);
@@ -372,16 +381,16 @@ hipError_t launch_quantize(const uint16_t* x, const uint16_t* up, int64_t rows, 
   const bool rot = group > 1;
   if (up != nullptr && rot)
     hipLaunchKernelGGL((quantize_kernel<true, true>), g1, dim3(kThreads), 0, s, x, up, rows, k, group, inv_sqrt_g,
-                       static_gsf, partials, n_partials, seg_rows, segments, codes, scales, gsf_out);
+                       static_gsf, partials, n_partials, seg_rows, segments, codes, scales, gsf_out, a16);
   else if (up != nullptr)
     hipLaunchKernelGGL((quantize_kernel<false, true>), g1, dim3(kThreads), 0, s, x, up, rows, k, group, inv_sqrt_g,
-                       static_gsf, partials, n_partials, seg_rows, segments, codes, scales, gsf_out);
+                       static_gsf, partials, n_partials, seg_rows, segments, codes, scales, gsf_out, a16);
   else if (rot)
     hipLaunchKernelGGL((quantize_kernel<true, false>), g1, dim3(kThreads), 0, s, x, up, rows, k, group, inv_sqrt_g,
-                       static_gsf, partials, n_partials, seg_rows, segments, codes, scales, gsf_out);
+                       static_gsf, partials, n_partials, seg_rows, segments, codes, scales, gsf_out, a16);
   else
     hipLaunchKernelGGL((quantize_kernel<false, false>), g1, dim3(kThreads), 0, s, x, up, rows, k, group, inv_sqrt_g,
-                       static_gsf, partials, n_partials, seg_rows, segments, codes, scales, gsf_out);
+                       static_gsf, partials, n_partials, seg_rows, segments, codes, scales, gsf_out, a16);
   return hipGetLastError();
 }
 
