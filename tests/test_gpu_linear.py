@@ -316,3 +316,49 @@ def test_static_decode_fused_quantize(m, n, k):
     assert np.array_equal(codes.cpu().numpy(), r["codes"])
     bound = accumulation_bound(o.dequantize(r["codes"], r["scales"]), o.dequantize(pw, sw), r["alpha"])
     assert_gemm_close(fused.float().cpu().numpy(), r["out"], bound)
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 4])
+@pytest.mark.parametrize("static,g", [(False, 0), (True, 0), (False, 16)])
+@pytest.mark.parametrize("n,k", [(1000, 4128), (5120, 1024)])
+def test_fp16_activation_decode_equals_codes_path(m, static, g, n, k):
+    """At most four rows nvfp4_linear hands the decode GEMM the quantized activation in
+    its fp16 operand form (code * scale * 2^-8) instead of codes and scales: the same
+    operands, so the output is bit-identical to quantizing first and running nvfp4_gemm,
+    and within tolerance of the oracle (partial last K tile with K = 4128)."""
+    x = workloads.draw("t3", (m, k), 7 * m + k, 0, 2.0)
+    w = workloads.draw("normal", (n, k), 41, n, 0.02)
+    bias = workloads.draw("normal", (n,), 42, n, 0.01)
+    # with a rotation the weight carries it, folded offline (bf16-exact values)
+    wf = o.fold_weight(w.float().numpy(), g) if g else w.float().numpy()
+    w_dev = torch.from_numpy(np.ascontiguousarray(wf, dtype=np.float32)).to(torch.bfloat16).to(DEV)
+    packed, inv_scale, gsf_w = nv().quantize_weight(w_dev)
+    xf = x.float().numpy()
+    gx = o.global_sf(o.amax(xf)) if static else None
+    gxt = None if gx is None else torch.tensor(float(gx), dtype=torch.float32, device=DEV)
+    out = nv().nvfp4_linear(x.to(DEV), packed, inv_scale, gsf_w, bias.to(DEV), n, gxt, g)
+    codes, scales, used = nv().quantize_activation(x.to(DEV), gxt, g)
+    two = nv().nvfp4_gemm(codes, scales, packed, inv_scale, used, gsf_w, bias.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(out, two)
+    pw, sw, gw = o.quantize_weight(wf)
+    r = o.nvfp4_linear_inference(xf, pw, sw, gw, bias.float().numpy(), gx, g)
+    assert np.array_equal(codes.cpu().numpy(), r["codes"])
+    bound = accumulation_bound(o.dequantize(r["codes"], r["scales"]), o.dequantize(pw, sw), r["alpha"])
+    assert_gemm_close(out.float().cpu().numpy(), r["out"], bound)
+
+
+@pytest.mark.parametrize("m", [1, 3])
+def test_fp16_activation_decode_swiglu(m):
+    """The SwiGLU linear at few rows takes the same fp16-activation decode path:
+    bit-identical to quantizing the product and running nvfp4_gemm."""
+    n, k = 640, 1024
+    gate = workloads.draw("normal", (m, k), 51 + m, 0, 1.0)
+    up = workloads.draw("normal", (m, k), 61 + m, 0, 1.0)
+    w = workloads.draw("normal", (n, k), 71, n, 0.02)
+    packed, inv_scale, gsf_w = nv().quantize_weight(w.to(DEV))
+    out = nv().nvfp4_linear_swiglu(gate.to(DEV), up.to(DEV), packed, inv_scale, gsf_w, None, n)
+    codes, scales, used = nv().quantize_swiglu(gate.to(DEV), up.to(DEV))
+    two = nv().nvfp4_gemm(codes, scales, packed, inv_scale, used, gsf_w, None)
+    torch.cuda.synchronize()
+    assert torch.equal(out, two)
