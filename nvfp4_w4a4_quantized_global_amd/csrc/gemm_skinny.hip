@@ -18,6 +18,9 @@
 // [64g + 8s, +8) of the super tile at sub-step s for both operands (a consistent
 // permutation of K), so each lane loads 32 contiguous code bytes per row and the 16
 // lanes of a row together read its whole 128-byte line.
+//
+// At most 16 rows take gemm_decode_kernel below instead: 16 columns per block, the
+// operands streamed through per-wave LDS slots by direct loads.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
