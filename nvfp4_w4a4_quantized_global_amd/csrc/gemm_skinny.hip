@@ -279,7 +279,7 @@ int skinny_splits(int64_t k, int64_t n, int cus) {
 // partials go to gemm_skinny_reduce.
 constexpr int kDecRows = 16;
 constexpr int kDecDepth = 2;                  // LDS slots (super tiles in flight) per wave
-constexpr int kDecSlot = 2 * 2048 + 2 * 256;  // B lines, A lines, B scale words, A scale words
+constexpr int kDecSlot = 2 * 2048 + 2 * 256;  // B lines, A lines (kA16: a16 rows), B and A scale words
 
 __device__ __forceinline__ int dec_swz(int r) { return (r >> 1) & 7; }
 
@@ -407,12 +407,11 @@ __global__ void __launch_bounds__(256) gemm_decode_kernel(
     }
   };
 
-  // Super tiles s0 + i and s0 + i + 1 from slots sa and sb.  The two slots are distinct
-  // and the restrict qualifiers tell the compiler so: reading one slot then does not
-  // wait for the direct loads still filling the other.
-  // The loop body has no branch (a merge point would make the compiler's wait tracking
-  // forget which slot a load fills); an odd last super tile is multiplied after it.
-  auto pair = [&](uint8_t* __restrict__ sa, uint8_t* __restrict__ sb, int i) __attribute__((always_inline)) {
+  // Super tiles s0 + i and s0 + i + 1 from slots sa and sb.  Each slot is refilled as
+  // soon as it has been multiplied, so one super tile's loads are in flight while the
+  // other is multiplied.  The loop body has no branch; an odd last super tile is
+  // multiplied after the loop.
+  auto pair = [&](uint8_t* sa, uint8_t* sb, int i) __attribute__((always_inline)) {
     dec_wait_one_behind<kLoads>();          // super tile s0 + i has landed
     multiply(sa, s0 + i);
     dec_lds_order();                // its reads are done before the slot is refilled
