@@ -128,6 +128,29 @@ def test_fused_rotation_equals_rotate_then_quantize(g):
     assert_same(gpu_quantize(x.cpu(), None, g), oracle_expected(x.cpu(), None, g), f"rot{g}")
 
 
+@pytest.mark.parametrize("m,k,g", [(4096, 5120, 0), (4096, 5248, 0), (4096, 4096, 16), (4096, 4224, 16),
+                                   (1, 16, 0), (37, 272, 0), (37, 272, 16), (300, 1024, 2), (513, 4224, 128)])
+def test_dynamic_equals_static_at_its_amax(m, k, g):
+    """The dynamic quantize (amax pass, then the quantize pass taking the max of the
+    partials) writes the same codes, scales and global scale as the static-scale pass
+    given the scale that the calibration kernels (nvfp4_amax, then
+    nvfp4_static_global_scale at margin 1) form from x: two kernel sequences that share
+    only the per-block encoder."""
+    print(f"[dynamic vs static quantize] {m}x{k} rot{g}", flush=True)
+    x = workloads.draw("t3", (m, k), 31, m + k + g).to(DEV)
+    gsf = nv().static_global_sf(nv().amax(x, g), 1.0)
+    dc, ds, dg = nv().quantize_activation(x, None, g)
+    sc, ss, sg = nv().quantize_activation(x, gsf, g)
+    torch.cuda.synchronize()
+    assert dg.item() == gsf.item() == sg.item()
+    assert torch.equal(ds, ss), f"{int((ds != ss).sum())} scale bytes differ"
+    assert torch.equal(dc, sc), f"{int((dc != sc).sum())} code bytes differ"
+    # and twice in a row: nothing carries over from one call to the next
+    dc2, ds2, dg2 = nv().quantize_activation(x, None, g)
+    torch.cuda.synchronize()
+    assert torch.equal(dc2, dc) and torch.equal(ds2, ds) and dg2.item() == dg.item()
+
+
 FULL = [
     ("qwen3 attention x [4096,5120]", lambda: workloads.qwen3_attention()[0].x, 0),
     ("qwen3 o_proj x [4096,8192]", lambda: workloads.qwen3_attention()[3].x, 0),
