@@ -47,6 +47,9 @@ def parse():
                    help="times the oracle runs the sample (the rate is the total work over the total time)")
     p.add_argument("--part", choices=("step", "gemm", "quantize", "copy"),
                    help="run only this part (warmup + steps launches, no JSON line): for counter runs")
+    p.add_argument("--decode", action="store_true",
+                   help="time the decode shapes instead (M = 1 and 16 on the k, q, gate and down projections; "
+                        "one line per shape, no JSON line)")
     p.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                    help="summarise rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of --part step and --part copy")
     return p.parse_args()
@@ -182,6 +185,75 @@ GEMM_KERNELS = ("::gemm_pipe_kernel<", "::split_k_reduce<")
 QUANT_KERNELS = ("::amax_partial_kernel<", "::quantize_kernel<")
 
 
+DECODE_PROJECTIONS = (("k", "self_attn.k_proj"), ("q", "self_attn.q_proj"), ("gate", "mlp.gate_proj"),
+                      ("down", "mlp.down_proj"))
+DECODE_COPIES = 4      # weight copies cycled: 4 x 73.7 MB exceeds the 256 MB last-level cache
+DECODE_REPS = 20
+
+
+def graph_time_us(fns, reps: int) -> float:
+    """Mean time per call of fns (run in turn, reps times) captured in one HIP graph,
+    so the host's launch cost is out of the figure."""
+    import torch
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(reps):
+                for f in fns:
+                    f()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    g.replay()
+    b.record()
+    b.synchronize()
+    return a.elapsed_time(b) / (reps * len(fns)) * 1e3
+
+
+def decode_table(nv, workloads, dev) -> None:
+    """The decode sweep's seeded inputs (x N(0,1), W N(0,0.02)); static scale = the one
+    calibrated on x itself (margin 1).  Columns: the static linear, the same as two
+    launches (quantize, then GEMM), the dynamic linear, and the GEMM alone."""
+    import torch
+    for short, name in DECODE_PROJECTIONS:
+        w = workloads.small_m_weight(name).to(dev)
+        n, k = w.shape
+        packed, inv_scale, gsf_w = nv.quantize_weight(w)
+        del w
+        copies = [(packed.clone(), inv_scale.clone()) for _ in range(DECODE_COPIES)]
+        for m in (1, 16):
+            x = workloads.small_m_input(m, name).to(dev)
+            gx = nv.static_global_sf(nv.amax(x), 1.0)
+            ws = torch.empty((nv.linear_workspace_bytes(m, k, n),), dtype=torch.uint8, device=dev)
+            gws = torch.empty((max(nv.gemm_workspace_bytes(m, k, n), 256),), dtype=torch.uint8, device=dev)
+            out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            codes, scales, _ = nv.quantize_activation(x, gx)
+
+            def two(p, sc):
+                c, s_, _ = nv.quantize_activation(x, gx)
+                nv.nvfp4_gemm(c, s_, p, sc, gx, gsf_w, None, out, gws)
+
+            cols = (
+                [lambda p=p, sc=sc: nv.nvfp4_linear(x, p, sc, gsf_w, None, n, gx, 0, ws, out) for p, sc in copies],
+                [lambda p=p, sc=sc: two(p, sc) for p, sc in copies],
+                [lambda p=p, sc=sc: nv.nvfp4_linear(x, p, sc, gsf_w, None, n, None, 0, ws, out) for p, sc in copies],
+                [lambda p=p, sc=sc: nv.nvfp4_gemm(codes, scales, p, sc, gx, gsf_w, None, out, gws) for p, sc in copies],
+            )
+            r = [graph_time_us(c, DECODE_REPS) for c in cols]
+            wbytes = n * k * 0.5625
+            print(f"{short:5s} M={m:2d}  [{n}x{k}]  static linear {r[0]:6.1f} us | static two launches {r[1]:6.1f} us"
+                  f" | dynamic linear {r[2]:6.1f} us | GEMM alone {r[3]:6.1f} us ({wbytes / r[3] / 1e6:4.2f} TB/s of"
+                  f" weight)", flush=True)
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -197,6 +269,9 @@ def main():
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
+    if args.decode:
+        decode_table(nv, workloads, dev)
+        return
     if args.part == "copy":
         # two plain copies of 1 GiB: the runtime's copy kernel, and torch's vectorised
         # elementwise kernel (16-byte loads and stores per lane, like the library's kernels)
