@@ -50,6 +50,9 @@ def parse():
     p.add_argument("--decode", action="store_true",
                    help="time the decode shapes instead (M = 1 and 16 on the k, q, gate and down projections; "
                         "one line per shape, no JSON line)")
+    p.add_argument("--tables", action="store_true",
+                   help="time the ViT-tile batch (per-tile calls vs one segmented call) and the down_proj SwiGLU "
+                        "front end (two steps vs fused) instead; one line per case, no JSON line")
     p.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                    help="summarise rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of --part step and --part copy")
     return p.parse_args()
@@ -254,6 +257,69 @@ def decode_table(nv, workloads, dev) -> None:
                   f" weight)", flush=True)
 
 
+def event_time_us(fn, iters: int = 10) -> float:
+    """Mean time per call of fn over iters back-to-back calls (HIP events), after 2 untimed."""
+    import torch
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        fn()
+    b.record()
+    b.synchronize()
+    return a.elapsed_time(b) / iters * 1e3
+
+
+def other_tables(nv, workloads, dev) -> None:
+    """8 ViT decoder tiles of 4096 tokens (rotation 16, one dynamic scale per tile): one
+    nvfp4_linear call per tile against one nvfp4_linear_segmented call; and the down_proj
+    input 4096 x 25600 formed from gate and up: swiglu then nvfp4_linear, against
+    nvfp4_linear_swiglu (front ends alone: swiglu + quantize vs quantize_swiglu)."""
+    import torch
+    for lin in workloads.vit_decoder_tiles(tiles=8):
+        x = lin.x.to(dev)
+        g = lin.rotation_group
+        tiles, rows = lin.meta["tiles"], lin.meta["tile_rows"]
+        wf = nv.rotate_activation(lin.w.to(dev).float(), g, out_dtype=torch.bfloat16)   # the offline fold
+        n, k = wf.shape
+        packed, inv_scale, gsf_w = nv.quantize_weight(wf)
+        del wf
+        out = torch.empty((tiles * rows, n), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty((nv.linear_workspace_bytes(rows, k, n),), dtype=torch.uint8, device=dev)
+        wss = torch.empty((nv.linear_segmented_workspace_bytes(tiles, rows, k, n),), dtype=torch.uint8, device=dev)
+
+        def per_tile():
+            for t in range(tiles):
+                nv.nvfp4_linear(x[t * rows:(t + 1) * rows], packed, inv_scale, gsf_w, None, n, None, g, ws,
+                                out[t * rows:(t + 1) * rows])
+
+        def segmented():
+            nv.nvfp4_linear_segmented(x, tiles, packed, inv_scale, gsf_w, None, n, g, wss, out)
+
+        a, b = event_time_us(per_tile), event_time_us(segmented)
+        print(f"vit {lin.name:6s} {tiles} tiles x [{rows},{k}] x [{n},{k}] rot{g}: per-tile calls {a:7.1f} us | "
+              f"segmented {b:7.1f} us ({a / b:.2f}x)", flush=True)
+        del x, packed, inv_scale, out
+    gate, up = (t.to(dev) for t in workloads.down_proj_gate_up())
+    w = workloads.qwen3_mlp(which=("down",))[0].w.to(dev)
+    n, k = w.shape
+    m = gate.shape[0]
+    packed, inv_scale, gsf_w = nv.quantize_weight(w)
+    del w
+    out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty((nv.linear_workspace_bytes(m, k, n),), dtype=torch.uint8, device=dev)
+    fr = (event_time_us(lambda: nv.quantize_activation(nv.swiglu(gate, up))),
+          event_time_us(lambda: nv.quantize_swiglu(gate, up)))
+    wh = (event_time_us(lambda: nv.nvfp4_linear(nv.swiglu(gate, up), packed, inv_scale, gsf_w, None, n, None, 0, ws,
+                                                out)),
+          event_time_us(lambda: nv.nvfp4_linear_swiglu(gate, up, packed, inv_scale, gsf_w, None, n, None, out=out)))
+    print(f"down_proj [{m},{k}] x [{n},{k}] dynamic: front end two steps {fr[0]:7.1f} us | fused {fr[1]:7.1f} us; "
+          f"whole linear two steps {wh[0]:7.1f} us | fused {wh[1]:7.1f} us", flush=True)
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -271,6 +337,9 @@ def main():
     stream = torch.cuda.current_stream(dev)
     if args.decode:
         decode_table(nv, workloads, dev)
+        return
+    if args.tables:
+        other_tables(nv, workloads, dev)
         return
     if args.part == "copy":
         # two plain copies of 1 GiB: the runtime's copy kernel, and torch's vectorised
