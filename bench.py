@@ -51,8 +51,9 @@ def parse():
                    help="time the decode shapes instead (M = 1 and 16 on the k, q, gate and down projections; "
                         "one line per shape, no JSON line)")
     p.add_argument("--tables", action="store_true",
-                   help="time the ViT-tile batch (per-tile calls vs one segmented call) and the down_proj SwiGLU "
-                        "front end (two steps vs fused) instead; one line per case, no JSON line")
+                   help="time the attention projections at 4096 rows, the ViT-tile batch (per-tile calls vs one "
+                        "segmented call) and the down_proj SwiGLU front end (two steps vs fused) instead; one line "
+                        "per case, no JSON line")
     p.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                    help="summarise rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of --part step and --part copy")
     return p.parse_args()
@@ -274,11 +275,30 @@ def event_time_us(fn, iters: int = 10) -> float:
 
 
 def other_tables(nv, workloads, dev) -> None:
-    """8 ViT decoder tiles of 4096 tokens (rotation 16, one dynamic scale per tile): one
+    """The attention projections at 4096 rows (q, k, v on one x [4096,5120], o on x
+    [4096,8192]): the dynamic linear and the GEMM alone.  8 ViT decoder tiles of 4096
+    tokens (rotation 16, one dynamic scale per tile): one
     nvfp4_linear call per tile against one nvfp4_linear_segmented call; and the down_proj
     input 4096 x 25600 formed from gate and up: swiglu then nvfp4_linear, against
     nvfp4_linear_swiglu (front ends alone: swiglu + quantize vs quantize_swiglu)."""
     import torch
+    for lin in workloads.qwen3_attention():
+        x = lin.x.to(dev)
+        m, k = x.shape
+        w = lin.w.to(dev)
+        n = w.shape[0]
+        packed, inv_scale, gsf_w = nv.quantize_weight(w)
+        del w
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty((nv.linear_workspace_bytes(m, k, n),), dtype=torch.uint8, device=dev)
+        gws = torch.empty((max(nv.gemm_workspace_bytes(m, k, n), 256),), dtype=torch.uint8, device=dev)
+        codes, scales, gx = nv.quantize_activation(x)
+        lt = event_time_us(lambda: nv.nvfp4_linear(x, packed, inv_scale, gsf_w, None, n, None, 0, ws, out))
+        gt = event_time_us(lambda: nv.nvfp4_gemm(codes, scales, packed, inv_scale, gx, gsf_w, None, out, gws))
+        fl = 2.0 * m * n * k
+        print(f"attn {lin.name:16s} [{m},{k}] x [{n},{k}] dynamic: linear {lt:7.1f} us ({fl / lt / 1e6:6.1f} TFLOP/s) | "
+              f"GEMM alone {gt:7.1f} us ({fl / gt / 1e6:6.1f} TFLOP/s)", flush=True)
+        del x, packed, inv_scale, out
     for lin in workloads.vit_decoder_tiles(tiles=8):
         x = lin.x.to(dev)
         g = lin.rotation_group
