@@ -408,7 +408,7 @@ def scale_from_canonical(canonical: torch.Tensor) -> torch.Tensor:
 class NVFP4Linear:
     """Inference-only NVFP4 W4A4 linear holding a packed weight.
 
-    Mirrors NVFP4DecoderLinear's frozen inference path: ``from_linear`` folds
+    Mirrors NVFP4DecoderLinear's frozen inference path: ``from_weight`` folds
     the optional block rotation into the weight in fp32, rounds it to bf16 and
     quantizes it once; ``__call__`` runs :func:`nvfp4_linear` with a dynamic
     (``act_scale='dynamic'``), static (``'static'``, 2688 / input_amax) or unit
