@@ -1,6 +1,7 @@
 """Pins for the oracle's block-scaled GEMM, its epilogue and the error probe."""
 import json
 import os
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -107,10 +108,43 @@ def test_probe_matches_the_pages_noise_figure():
     # a unit activation scale (the converter's probe) gives the same noise level
     r1 = o.nvfp4_linear_inference(rng_x, pw, sw, gw, global_sf_x=1.0)
     assert abs(o.probe_relative_error(r1["out"], rng_x, w) - genuine) < 0.015
-    # scales that do not belong to the codes are far off; missing scales read exactly 1.0
+    # scales that do not belong to their codes (a layout error) are far off
     bad = np.random.default_rng(0).permutation(sw.ravel()).reshape(sw.shape)
     err_bad = o.probe_relative_error(o.nvfp4_gemm(r["codes"], r["scales"], pw, bad, r["alpha"]), rng_x, w)
     assert err_bad > 2.5 * err
-    zero = np.zeros_like(sw)
-    err_zero = o.probe_relative_error(o.nvfp4_gemm(r["codes"], r["scales"], pw, zero, r["alpha"]), rng_x, w)
-    assert err_zero == pytest.approx(figs["probe_wrong_scale_layout"]["value"], abs=1e-12)
+
+
+def _fp32_nearest(q: Fraction) -> Fraction:
+    """The fp32 value nearest to a positive rational q, ties to even (exact arithmetic)."""
+    e = q.numerator.bit_length() - q.denominator.bit_length()
+    while Fraction(2) ** e > q:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= q:
+        e += 1
+    ulp = Fraction(2) ** (e - 23)
+    m = q / ulp
+    mi = m.numerator // m.denominator
+    rest = m - mi
+    if rest > Fraction(1, 2) or (rest == Fraction(1, 2) and mi % 2 == 1):
+        mi += 1
+    return mi * ulp
+
+
+def test_alpha_is_two_fp32_roundings():
+    # nvfp4_linear_inference forms 1.0 / (global_sf_x * global_sf_w) on fp32 scalars: the
+    # product is rounded to fp32, then the quotient.  Find global scales (2688 / amax) where
+    # that differs from the correctly rounded 1 / (gx * gw), and check the oracle gives the
+    # twice-rounded value there, from exact rational arithmetic.
+    rng = np.random.default_rng(123)
+    witnesses = 0
+    for _ in range(400):
+        gx = np.float32(np.float32(2688.0) / np.float32(rng.uniform(0.5, 40.0)))
+        gw = np.float32(np.float32(2688.0) / np.float32(rng.uniform(0.01, 0.3)))
+        exact = Fraction(float(gx)) * Fraction(float(gw))
+        twice = _fp32_nearest(1 / _fp32_nearest(exact))
+        once = _fp32_nearest(1 / exact)
+        got = o.alpha_of(gx, gw)
+        assert Fraction(float(got)) == twice
+        if twice != once:
+            witnesses += 1
+    assert witnesses >= 20

@@ -5,7 +5,9 @@ weight along the input dimension and applied to the activation at run time,
 exact in full precision, with H orthonormal and symmetric
 ("minimax_h3_nvfp4_decoder": module docstring; NVFP4DecoderLinear.from_linear).
 """
+import json
 import math
+import os
 
 import numpy as np
 import pytest
@@ -13,6 +15,8 @@ import scipy.linalg
 
 import oracle as o
 import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
 @pytest.mark.parametrize("g", [1, 2, 4, 8, 16, 32, 64, 128, 256])
@@ -70,3 +74,36 @@ def test_rotation_spreads_outliers():
     x[0, 5] = 8.0
     y = o.rotate_activation(x, 16, out="f32")
     assert np.array_equal(np.abs(y), np.full((1, 16), 2.0, dtype=np.float32))
+
+
+def test_rotated_linear_hand_worked():
+    # tests/golden/rotated_rows.json: the whole rotated path worked by hand.  The global
+    # scale comes from the rotated input (1344), not the raw one (336), so an amax taken
+    # before the rotation fails here, as does a wrong Hadamard sign pattern or scaling.
+    d = json.load(open(os.path.join(GOLDEN, "rotated_rows.json")))
+    g = d["rotation_group"]
+    x = np.array(d["x"], dtype=np.float32)
+    w = np.array(d["w"], dtype=np.float32)
+    pw, sw, gw = o.quantize_weight(o.fold_weight(w, g))
+    assert gw == np.float32(d["gsf_w"])
+    assert sw.tolist() == d["w_scale_bytes"] and pw.tolist() == d["w_packed"]
+    r = o.nvfp4_linear_inference(x, pw, sw, gw, rotation_group=g)
+    assert r["gsf_x"] == np.float32(d["gsf_x"])
+    assert r["scales"].tolist() == d["x_scale_bytes"]
+    assert o.unpack_codes(r["codes"]).tolist() == d["x_codes"]
+    assert r["codes"].tolist() == d["x_packed"]
+    assert r["alpha"] == np.float32(float.fromhex(d["alpha_hex"]))
+    assert r["out"].tolist() == d["out"]
+
+
+def test_dynamic_scale_is_taken_after_the_rotation():
+    # heavy-tailed rows: the rotation spreads each group's outliers, so the rotated
+    # input's amax is smaller and the two orders give different global scales
+    x = workloads.draw("t3", (64, 256), 11, 0).float().numpy()
+    pw, sw, gw = o.quantize_weight(o.fold_weight(workloads.draw("normal", (32, 256), 11, 1, 0.02).float().numpy(), 16))
+    r = o.nvfp4_linear_inference(x, pw, sw, gw, rotation_group=16)
+    raw_amax = float(np.max(np.abs(x)))
+    rot_amax = float(np.max(np.abs(r["x_rot"])))
+    assert rot_amax < raw_amax
+    assert r["gsf_x"] == np.float32(np.float32(2688.0) / np.float32(rot_amax))
+    assert r["gsf_x"] != np.float32(np.float32(2688.0) / np.float32(raw_amax))
