@@ -62,9 +62,17 @@ enum { NVFP4_DTYPE_BF16 = 0, NVFP4_DTYPE_F32 = 1 };
 #define NVFP4_MAX_ROTATION_GROUP 128
 #define NVFP4_WORKSPACE_ALIGN 256
 
-/* Every bf16 / fp32 activation, weight or output tensor passed to the library must
- * be 16-byte aligned (misaligned pointers are rejected with NVFP4_ERR_ARG); packed
- * codes and scales follow the alignment each call states. */
+/* Alignment.  Every call checks its pointers and returns NVFP4_ERR_ARG for a misaligned
+ * one, before anything is queued:
+ *   - bf16 / fp32 inputs (x, w, gate, up, rotate_activation's x and y, nvfp4_swiglu's
+ *     x, nvfp4_dequantize's out): 16 bytes;
+ *   - packed codes and block-scale arrays (packed, inv_scale, codes, scales, x_codes,
+ *     x_scale): 8 bytes (nvfp4_dequantize reads its scales byte by byte: any address);
+ *   - bf16 outputs and biases of the linear and GEMM calls (out, bias): 2 bytes (the
+ *     kernels take wide stores and loads only where the address allows them);
+ *   - fp32 scalars (global scales, gsf_out, amax): 4 bytes;
+ *   - workspaces: NVFP4_WORKSPACE_ALIGN.
+ * The scale-layout converters access bytes and need no alignment. */
 
 /* Bytes of a block-scale array for a [rows, k] tensor in the layout above. */
 size_t nvfp4_scale_bytes(int64_t rows, int64_t k);

@@ -54,10 +54,29 @@ int check_group(const char* fn, int g, int64_t k, bool allow_none) {
 
 float inv_sqrt(int g) { return g > 1 ? (float)(1.0 / sqrt((double)g)) : 1.0f; }
 
-// The kernels read and write rows in 16-byte pieces.
-int check_aligned(const char* fn, const char* what, const void* p) {
-  if ((uintptr_t)p % 16) return fail(NVFP4_ERR_ARG, "%s: %s must be 16-byte aligned", fn, what);
+// Alignment the kernels rely on: bf16 / fp32 inputs are read in 16-byte pieces, codes
+// and scales in 8-byte pieces, outputs and biases element by element wherever a wider
+// access would be misaligned, global scales as fp32 words.  NULL passes (optional
+// pointers are checked for presence elsewhere).
+int check_align(const char* fn, const char* what, const void* p, unsigned bytes) {
+  if ((uintptr_t)p % bytes) return fail(NVFP4_ERR_ARG, "%s: %s must be %u-byte aligned", fn, what, bytes);
   return NVFP4_OK;
+}
+int check_aligned(const char* fn, const char* what, const void* p) { return check_align(fn, what, p, 16); }
+
+// Packed codes and block scales of one operand (8-byte pieces).
+int check_nvfp4_operand(const char* fn, const char* codes_name, const void* codes, const char* scales_name,
+                        const void* scales) {
+  if (int rc = check_align(fn, codes_name, codes, 8)) return rc;
+  return check_align(fn, scales_name, scales, 8);
+}
+
+// bf16 output and optional bias (element alignment), fp32 global scales.
+int check_epilogue(const char* fn, const void* out, const void* bias, const float* gsf_a, const float* gsf_b) {
+  if (int rc = check_align(fn, "out", out, 2)) return rc;
+  if (int rc = check_align(fn, "bias", bias, 2)) return rc;
+  if (int rc = check_align(fn, "global_sf_x", gsf_a, 4)) return rc;
+  return check_align(fn, "global_sf_w", gsf_b, 4);
 }
 
 struct LinearWorkspace {
@@ -74,14 +93,16 @@ struct LinearWorkspace {
 // Layout of an nvfp4_linear workspace: codes, scales, amax partials, one global scale
 // per segment, the GEMM's split-K partials, then (m <= kDecodeA16Rows) the fp16 operand
 // form of the activation for the decode GEMM; every piece 256-byte aligned.
-LinearWorkspace carve(void* base, int64_t m, int64_t k, int64_t n, int64_t segments = 1) {
+// Without split_k the GEMM region is left out (the GEMM then runs its last round of
+// tiles unsplit: the same function, fp32 summation order aside).
+LinearWorkspace carve(void* base, int64_t m, int64_t k, int64_t n, int64_t segments = 1, bool split_k = true) {
   // offsets first, pointers only for a real base
   const size_t o_codes = 0;
   const size_t o_scales = align_up(o_codes + (size_t)m * (size_t)(k / 2));
   const size_t o_partials = align_up(o_scales + nvfp4_scale_bytes(m, k));
   const size_t o_gsf = align_up(o_partials + sizeof(float) * nvfp4::kMaxAmaxPartials);
   const size_t o_gemm = align_up(o_gsf + sizeof(float) * (size_t)segments);
-  const size_t gemm_bytes = nvfp4::gemm_workspace_bytes(m, k, n);
+  const size_t gemm_bytes = split_k ? nvfp4::gemm_workspace_bytes(m, k, n) : 0;
   const size_t o_a16 = align_up(o_gemm + gemm_bytes);
   const size_t a16_bytes = m <= nvfp4::kDecodeA16Rows && segments == 1 ? (size_t)m * (size_t)k * 2u : 0;
   LinearWorkspace w{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, gemm_bytes, align_up(o_a16 + a16_bytes)};
@@ -140,7 +161,7 @@ int check_segments(const char* fn, int64_t segments, int64_t seg_rows) {
 int linear_impl(const char* fn, const void* x, int64_t segments, int64_t seg_rows, int64_t k, const uint8_t* packed,
                 const uint8_t* inv_scale, const float* global_sf_w, const void* bias, int64_t out_features,
                 const float* global_sf_x, int rotation_group, void* out, float* gsf_out, void* workspace,
-                size_t workspace_bytes, hipStream_t s, const void* up = nullptr) {
+                size_t workspace_bytes, hipStream_t s, const void* up = nullptr, bool split_k = true) {
   // a dynamic scale over a SwiGLU product keeps the product after the linear workspace
   const bool keep_product = up != nullptr && global_sf_x == nullptr;
   const int64_t m = segments * seg_rows;
@@ -151,12 +172,15 @@ int linear_impl(const char* fn, const void* x, int64_t segments, int64_t seg_row
   if (m == 0) return NVFP4_OK;
   if (!x || !packed || !inv_scale || !global_sf_w || !out) return fail(NVFP4_ERR_ARG, "%s: NULL tensor argument", fn);
   if (int rc = check_aligned(fn, "x", x)) return rc;
-  const size_t base = carve(nullptr, m, k, out_features, segments).bytes;
+  if (int rc = check_nvfp4_operand(fn, "packed", packed, "inv_scale", inv_scale)) return rc;
+  if (int rc = check_epilogue(fn, out, bias, global_sf_x, global_sf_w)) return rc;
+  if (int rc = check_align(fn, "gsf_out", gsf_out, 4)) return rc;
+  const size_t base = carve(nullptr, m, k, out_features, segments, split_k).bytes;
   const size_t need = base + (keep_product ? product_bytes(m, k) : 0);
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % NVFP4_WORKSPACE_ALIGN))
     return fail(NVFP4_ERR_WORKSPACE, "%s: need a %d-byte aligned workspace of %zu bytes, got %zu", fn,
                 NVFP4_WORKSPACE_ALIGN, need, workspace_bytes);
-  const LinearWorkspace ws = carve(workspace, m, k, out_features, segments);
+  const LinearWorkspace ws = carve(workspace, m, k, out_features, segments, split_k);
   if (global_sf_x != nullptr && rotation_group == 0 && up == nullptr && segments == 1 && gsf_out == nullptr &&
       nvfp4::linear_skinny_fused_supported(m, k, out_features, x, packed, inv_scale, nvfp4::compute_units()) &&
       ws.gemm_bytes >= nvfp4::gemm_workspace_bytes(m, k, out_features)) {
@@ -254,6 +278,8 @@ int nvfp4_quantize_weight(const void* w, int64_t n, int64_t k, uint8_t* packed, 
   if (int rc = check_rows_k(fn, n, k, false)) return rc;
   if (!w || !packed || !inv_scale || !global_sf_w) return fail(NVFP4_ERR_ARG, "%s: NULL tensor argument", fn);
   if (int rc = check_aligned(fn, "w", w)) return rc;
+  if (int rc = check_nvfp4_operand(fn, "packed", packed, "inv_scale", inv_scale)) return rc;
+  if (int rc = check_align(fn, "global_sf_w", global_sf_w, 4)) return rc;
   if (!workspace || workspace_bytes < nvfp4_quantize_workspace_bytes() ||
       ((uintptr_t)workspace % NVFP4_WORKSPACE_ALIGN))
     return fail(NVFP4_ERR_WORKSPACE, "%s: need a %d-byte aligned workspace of %zu bytes, got %zu", fn,
@@ -272,6 +298,9 @@ int nvfp4_quantize_activation(const void* x, int64_t m, int64_t k, const float* 
   if (m == 0) return NVFP4_OK;
   if (!x || !codes || !scales) return fail(NVFP4_ERR_ARG, "%s: NULL tensor argument", fn);
   if (int rc = check_aligned(fn, "x", x)) return rc;
+  if (int rc = check_nvfp4_operand(fn, "codes", codes, "scales", scales)) return rc;
+  if (int rc = check_align(fn, "global_sf_x", global_sf_x, 4)) return rc;
+  if (int rc = check_align(fn, "gsf_out", gsf_out, 4)) return rc;
   if (global_sf_x == nullptr &&
       (!workspace || workspace_bytes < nvfp4_quantize_workspace_bytes() ||
        ((uintptr_t)workspace % NVFP4_WORKSPACE_ALIGN)))
@@ -288,6 +317,7 @@ int nvfp4_amax(const void* x, int64_t rows, int64_t k, int rotation_group, float
   if (int rc = check_rows_k(fn, rows, k, true)) return rc;
   if (int rc = check_group(fn, rotation_group, k, true)) return rc;
   if (!amax) return fail(NVFP4_ERR_ARG, "%s: amax must not be NULL", fn);
+  if (int rc = check_align(fn, "amax", amax, 4)) return rc;
   if (rows > 0 && !x) return fail(NVFP4_ERR_ARG, "%s: x must not be NULL", fn);
   if (rows > 0)
     if (int rc = check_aligned(fn, "x", x)) return rc;
@@ -329,6 +359,9 @@ int nvfp4_quantize_swiglu(const void* gate, const void* up, int64_t m, int64_t k
   if (m == 0) return NVFP4_OK;
   if (!gate || !up || !codes || !scales) return fail(NVFP4_ERR_ARG, "%s: NULL tensor argument", fn);
   if (((uintptr_t)gate | (uintptr_t)up) % 16) return fail(NVFP4_ERR_ARG, "%s: gate and up must be 16-byte aligned", fn);
+  if (int rc = check_nvfp4_operand(fn, "codes", codes, "scales", scales)) return rc;
+  if (int rc = check_align(fn, "global_sf_x", global_sf_x, 4)) return rc;
+  if (int rc = check_align(fn, "gsf_out", gsf_out, 4)) return rc;
   const size_t need = nvfp4_quantize_swiglu_workspace_bytes(m, k);
   if (global_sf_x == nullptr &&
       (!workspace || workspace_bytes < need || ((uintptr_t)workspace % NVFP4_WORKSPACE_ALIGN)))
@@ -361,6 +394,7 @@ int nvfp4_dequantize(const uint8_t* packed, const uint8_t* scales, int64_t rows,
   if (!packed || !scales || !global_sf || !out) return fail(NVFP4_ERR_ARG, "%s: NULL argument", fn);
   if (((uintptr_t)packed % 8) || ((uintptr_t)out % 16))
     return fail(NVFP4_ERR_ARG, "%s: packed must be 8-byte and out 16-byte aligned", fn);
+  if (int rc = check_align(fn, "global_sf", global_sf, 4)) return rc;
   return hip_status(nvfp4::launch_dequant(packed, scales, rows, k, global_sf, out, out_dtype == NVFP4_DTYPE_BF16,
                                           static_cast<hipStream_t>(stream)),
                     fn);
@@ -370,6 +404,8 @@ int nvfp4_static_global_scale(const float* amax, float margin, float* gsf, void*
   const char* fn = "nvfp4_static_global_scale";
   g_err[0] = 0;
   if (!amax || !gsf) return fail(NVFP4_ERR_ARG, "%s: NULL argument", fn);
+  if (int rc = check_align(fn, "amax", amax, 4)) return rc;
+  if (int rc = check_align(fn, "gsf", gsf, 4)) return rc;
   if (!(margin > 0.0f) || margin != margin || margin > 3.0e38f)
     return fail(NVFP4_ERR_ARG, "%s: margin must be a positive finite number", fn);
   return hip_status(nvfp4::launch_static_scale(amax, margin, gsf, static_cast<hipStream_t>(stream)), fn);
@@ -387,6 +423,8 @@ int nvfp4_quantize_activation_segmented(const void* x, int64_t segments, int64_t
   if (m == 0) return NVFP4_OK;
   if (!x || !codes || !scales || !gsf_out) return fail(NVFP4_ERR_ARG, "%s: NULL tensor argument", fn);
   if (int rc = check_aligned(fn, "x", x)) return rc;
+  if (int rc = check_nvfp4_operand(fn, "codes", codes, "scales", scales)) return rc;
+  if (int rc = check_align(fn, "gsf_out", gsf_out, 4)) return rc;
   if (!workspace || workspace_bytes < nvfp4_quantize_workspace_bytes() ||
       ((uintptr_t)workspace % NVFP4_WORKSPACE_ALIGN))
     return fail(NVFP4_ERR_WORKSPACE, "%s: need a %d-byte aligned workspace of %zu bytes", fn, NVFP4_WORKSPACE_ALIGN,
@@ -405,6 +443,9 @@ int nvfp4_gemm(const uint8_t* x_codes, const uint8_t* x_scale, int64_t m, int64_
   if (m == 0) return NVFP4_OK;
   if (!x_codes || !x_scale || !packed || !inv_scale || !gsf_x || !gsf_w || !out)
     return fail(NVFP4_ERR_ARG, "%s: NULL tensor argument", fn);
+  if (int rc = check_nvfp4_operand(fn, "x_codes", x_codes, "x_scale", x_scale)) return rc;
+  if (int rc = check_nvfp4_operand(fn, "packed", packed, "inv_scale", inv_scale)) return rc;
+  if (int rc = check_epilogue(fn, out, bias, gsf_x, gsf_w)) return rc;
   if (workspace != nullptr && ((uintptr_t)workspace % NVFP4_WORKSPACE_ALIGN))
     return fail(NVFP4_ERR_WORKSPACE, "%s: workspace must be %d-byte aligned", fn, NVFP4_WORKSPACE_ALIGN);
   return hip_status(nvfp4::launch_gemm(x_codes, x_scale, m, k, packed, inv_scale, n, gsf_x, gsf_w, 0,

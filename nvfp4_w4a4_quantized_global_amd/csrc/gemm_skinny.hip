@@ -287,14 +287,13 @@ __device__ __forceinline__ int dec_swz(int r) { return (r >> 1) & 7; }
 // dst is wave-uniform and goes to M0).  Written as inline asm so that the compiler does
 // not track these loads: it would otherwise make every LDS read of the ring wait for all
 // of them (it cannot tell the slots apart across loop iterations).  The kernel waits for
-// them itself (dec_wait_*), and nothing else in it uses M0.
+// them itself (dec_wait_*).  The LDS address is an M0 input operand, so the compiler
+// itself sets M0 and knows what it holds.
 __device__ __forceinline__ void dec_dma16(const uint8_t* src, uint8_t* dst) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"((uint32_t)(uintptr_t)dst), "v"(src) : "memory");
+  asm volatile("global_load_lds_dwordx4 %1, off" :: "{m0}"((uint32_t)(uintptr_t)dst), "v"(src) : "memory");
 }
 __device__ __forceinline__ void dec_dma4(const uint8_t* src, uint8_t* dst) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
-               :: "s"((uint32_t)(uintptr_t)dst), "v"(src) : "memory");
+  asm volatile("global_load_lds_dword %1, off" :: "{m0}"((uint32_t)(uintptr_t)dst), "v"(src) : "memory");
 }
 // Waits until at most one super tile's kLoads direct loads (the newer one) are in
 // flight; the compiler moves no memory access across it.

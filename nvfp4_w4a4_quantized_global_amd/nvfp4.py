@@ -9,6 +9,7 @@ the "minimax_h3_nvfp4_decoder" page: ``rotate_activation``,
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 
 import torch
@@ -405,120 +406,155 @@ def scale_from_canonical(canonical: torch.Tensor) -> torch.Tensor:
     return out[: scale_bytes(rows, k)]
 
 
-class NVFP4Linear:
-    """Inference-only NVFP4 W4A4 linear holding a packed weight.
+def _check_layer_geometry(packed: torch.Tensor, in_features: int, rotation_group: int | None) -> None:
+    """A packed NVFP4 weight must hold whole 16-value blocks of every row, and a rotation
+    group must tile the input dimension exactly."""
+    if in_features <= 0 or in_features % NVFP4_BLOCK_SIZE:
+        raise ValueError(f"in_features={in_features}: an NVFP4 row is made of whole blocks of "
+                         f"{NVFP4_BLOCK_SIZE} values")
+    if rotation_group is not None and (rotation_group < 2 or in_features % rotation_group):
+        raise ValueError(f"rotation_group={rotation_group} must be at least 2 and split in_features={in_features} "
+                         "into whole groups")
+    if packed.dtype != torch.uint8 or packed.dim() != 2 or packed.shape[1] * 2 != in_features:
+        raise ValueError(f"packed NVFP4 weight: expected a 2-D uint8 tensor with in_features / 2 = "
+                         f"{in_features // 2} bytes per row, got {packed.dtype} {list(packed.shape)}")
 
-    Mirrors NVFP4DecoderLinear's frozen inference path: ``from_weight`` folds
-    the optional block rotation into the weight in fp32, rounds it to bf16 and
-    quantizes it once; ``__call__`` runs :func:`nvfp4_linear` with a dynamic
-    (``act_scale='dynamic'``), static (``'static'``, 2688 / input_amax) or unit
-    (``'unit'``) activation scale.
+
+class NVFP4Linear:
+    """An inference NVFP4 W4A4 linear over a packed weight.
+
+    The interface follows NVFP4DecoderLinear on the "minimax_h3_nvfp4_decoder" page
+    (frozen inference path, ``act_scale`` modes, optional block rotation, per-tile use
+    by the decoder): ``from_weight`` folds the rotation into the weight in fp32, rounds
+    it to bf16 and packs it once; calling the layer runs :func:`nvfp4_linear` with the
+    activation scale of its mode:
+
+    * ``"dynamic"``: from the abs-max of each call's input (after the rotation);
+    * ``"static"``: ``2688 / (input_amax * margin)``, fixed;
+    * ``"unit"``: 1.
+
+    A static scale is usually measured with :func:`calibration` (or
+    :func:`calibrate_static_scales`).
     """
 
-    ACT_SCALES = ("dynamic", "static", "unit")
+    SCALE_MODES = ("dynamic", "static", "unit")
+    ACT_SCALES = SCALE_MODES
 
     def __init__(self, packed, inv_scale, global_sf_w, bias, in_features, rotation_group=None,
                  act_scale="dynamic", input_amax=None, margin: float = 1.0):
-        if in_features % NVFP4_BLOCK_SIZE:
-            raise ValueError(f"NVFP4 needs in_features divisible by {NVFP4_BLOCK_SIZE}, got {in_features}")
-        if rotation_group is not None and in_features % rotation_group:
-            raise ValueError(f"rotation group {rotation_group} does not divide in_features {in_features}")
-        if act_scale not in self.ACT_SCALES:
-            raise ValueError(f"act_scale must be one of {self.ACT_SCALES}, got {act_scale!r}")
-        if packed.dtype != torch.uint8 or packed.shape[1] * 2 != in_features:
-            raise ValueError(f"packed NVFP4 weight must be uint8 [{packed.shape[0]}, {in_features // 2}], "
-                             f"got {packed.dtype} {list(packed.shape)}")
-        self.packed, self.inv_scale, self.global_sf_w = packed, inv_scale, global_sf_w
+        if act_scale not in self.SCALE_MODES:
+            raise ValueError(f"unknown activation-scale mode {act_scale!r}; the modes are {self.SCALE_MODES}")
+        _check_layer_geometry(packed, int(in_features), rotation_group)
+        self.packed = packed
+        self.inv_scale = inv_scale
+        self.global_sf_w = global_sf_w
         self.bias = bias
-        self.in_features = in_features
+        self.in_features = int(in_features)
         self.out_features = packed.shape[0]
         self.rotation_group = rotation_group
         self.act_scale = act_scale
         self.input_amax = input_amax
         self.margin = float(margin)
-        self.calibrating = False
-        self._gsf_x = None
+        self._gsf_x = None      # cached static / unit scale (fp32 0-d device tensor)
+        self._record = None     # running abs-max while a calibration is open
 
     @classmethod
     def from_weight(cls, weight: torch.Tensor, bias: torch.Tensor | None = None, rotation_group: int | None = None,
                     act_scale: str = "dynamic", input_amax=None) -> "NVFP4Linear":
-        """weight: [out, in] on the GPU (any float dtype; the fold runs in fp32)."""
-        out_f, in_f = weight.shape
-        if in_f % NVFP4_BLOCK_SIZE:
-            raise ValueError(f"NVFP4 needs in_features divisible by {NVFP4_BLOCK_SIZE}, got {in_f}")
-        if rotation_group is not None:
-            if in_f % rotation_group:
-                raise ValueError(f"rotation group {rotation_group} does not divide in_features {in_f}")
-            w = rotate_activation(weight.float().contiguous(), rotation_group, out_dtype=torch.bfloat16)
-        else:
+        """Pack a full-precision weight [out, in] that lives on the GPU (any float dtype)."""
+        if weight.dim() != 2:
+            raise ValueError(f"weight must be [out_features, in_features], got shape {list(weight.shape)}")
+        in_f = weight.shape[1]
+        if in_f % NVFP4_BLOCK_SIZE or (rotation_group is not None and in_f % rotation_group):
+            # the same message the constructor gives, before any work on the device
+            _check_layer_geometry(torch.empty((0, in_f // 2), dtype=torch.uint8), in_f, rotation_group)
+        if rotation_group is None:
             w = weight.to(torch.bfloat16).contiguous()
+        else:
+            w = rotate_activation(weight.float().contiguous(), rotation_group, out_dtype=torch.bfloat16)
         packed, inv_scale, gsf_w = quantize_weight(w)
         b = None if bias is None else bias.to(torch.bfloat16).contiguous()
         return cls(packed, inv_scale, gsf_w, b, in_f, rotation_group, act_scale, input_amax)
 
+    @property
+    def calibrating(self) -> bool:
+        return self._record is not None
+
     def activation_global_sf(self):
+        """The fixed activation scale of a static or unit layer (None when dynamic)."""
         if self.act_scale == "dynamic":
             return None
         if self._gsf_x is None:
+            dev = self.packed.device
             if self.act_scale == "unit":
-                self._gsf_x = torch.ones((), dtype=torch.float32, device=self.packed.device)
+                self._gsf_x = torch.ones((), dtype=torch.float32, device=dev)
+            elif self.input_amax is None:
+                raise ValueError("a static activation scale needs input_amax (set it or run a calibration)")
             else:
-                if self.input_amax is None:
-                    raise ValueError("act_scale='static' needs input_amax")
-                amax_t = torch.as_tensor(self.input_amax, dtype=torch.float32, device=self.packed.device).reshape(())
-                self._gsf_x = static_global_sf(amax_t.contiguous(), self.margin)
+                peak = torch.as_tensor(self.input_amax, dtype=torch.float32, device=dev).reshape(())
+                self._gsf_x = static_global_sf(peak.contiguous(), self.margin)
         return self._gsf_x
 
-    # Calibration of a static scale ("minimax_h3_nvfp4_decoder" page,
-    # calibrate_static_scales): record the running abs-max of the (rotated) inputs
-    # while running with dynamic numerics, then switch to the static scale.
-    def start_calibration(self) -> None:
-        self._record = torch.zeros((), dtype=torch.float32, device=self.packed.device)
-        self.calibrating = True
-
-    def finish_calibration(self, margin: float = 1.0) -> None:
-        self.calibrating = False
-        if not float(self._record.item()) > 0.0:
-            raise RuntimeError("an NVFP4 linear saw no activations during calibration")
-        self.input_amax, self.margin, self.act_scale, self._gsf_x = self._record, float(margin), "static", None
+    def use_static_scale(self, input_amax, margin: float = 1.0) -> None:
+        """Switch to a static scale from a recorded abs-max (a float or an fp32 device scalar)."""
+        self.act_scale, self.input_amax, self.margin, self._gsf_x = "static", input_amax, float(margin), None
 
     def __call__(self, x: torch.Tensor) -> torch.Tensor:
         x = x.to(torch.bfloat16)
-        if self.calibrating:
-            amax(x, self.rotation_group or 0, out=self._record, accumulate=True)
-            return nvfp4_linear(x, self.packed, self.inv_scale, self.global_sf_w, self.bias, self.out_features, None,
-                                self.rotation_group or 0)
-        return nvfp4_linear(x, self.packed, self.inv_scale, self.global_sf_w, self.bias,
-                            self.out_features, self.activation_global_sf(), self.rotation_group or 0)
+        g = self.rotation_group or 0
+        if self._record is not None:
+            # calibration: dynamic numerics, and the rotated input's abs-max raises the record
+            amax(x, g, out=self._record, accumulate=True)
+            gsf = None
+        else:
+            gsf = self.activation_global_sf()
+        return nvfp4_linear(x, self.packed, self.inv_scale, self.global_sf_w, self.bias, self.out_features, gsf, g)
 
     def dequantized_weight(self, dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
         """The packed weight expanded back to ``dtype`` (the W4A16 fallback's weight)."""
         return dequantize(self.packed, self.inv_scale, self.global_sf_w, dtype)
 
     def forward_tiles(self, x: torch.Tensor, tiles: int) -> torch.Tensor:
-        """x holds ``tiles`` equal row blocks (decoder tiles); one pass over all of them
-        with the result of calling the layer on each tile alone.  With a dynamic scale
-        every tile keeps its own global scale; static and unit scales are shared anyway."""
-        if self.calibrating:
-            return self(x)
-        if self.act_scale != "dynamic":
+        """``x`` holds ``tiles`` equal row blocks (decoder tiles).  One pass gives what calling
+        the layer on each tile alone gives: with a dynamic scale every tile keeps its own
+        global scale; a static or unit scale is shared by all tiles anyway."""
+        if self.act_scale != "dynamic" or self._record is not None:
             return self(x)
         return nvfp4_linear_segmented(x.to(torch.bfloat16), tiles, self.packed, self.inv_scale, self.global_sf_w,
                                       self.bias, self.out_features, self.rotation_group or 0)
 
 
-def calibrate_static_scales(layers, run_batches, margin: float = 1.0) -> int:
-    """Record every layer's activation abs-max over ``run_batches()`` (dynamic numerics
-    while recording), then switch the layers to static scales with ``margin`` applied
-    to the recorded range; returns the number of layers."""
+@contextlib.contextmanager
+def calibration(layers, margin: float = 1.0):
+    """Measure static activation scales for ``layers`` over the code run inside the block.
+
+    While the block runs, each layer keeps its dynamic scale and raises a running abs-max
+    of its (rotated) inputs on the device.  When the block finishes without an exception,
+    every layer switches to the static scale ``2688 / (abs-max * margin)``; a layer whose
+    record is still 0 raises RuntimeError.  The block receives the list of layers.
+    """
     layers = list(layers)
     for layer in layers:
-        layer.start_calibration()
+        layer._record = torch.zeros((), dtype=torch.float32, device=layer.packed.device)
     try:
-        run_batches()
+        yield layers
     finally:
+        records = [layer._record for layer in layers]
         for layer in layers:
-            layer.calibrating = False
-    for layer in layers:
-        layer.finish_calibration(margin)
-    return len(layers)
+            layer._record = None
+    peaks = torch.stack(records).cpu().tolist() if records else []
+    empty = [i for i, p in enumerate(peaks) if not p > 0.0]
+    if empty:
+        raise RuntimeError(f"calibration: layer(s) {empty} recorded no nonzero activation, so no static scale "
+                           "can be formed")
+    for layer, rec in zip(layers, records):
+        layer.use_static_scale(rec, margin)
+
+
+def calibrate_static_scales(layers, run_batches, margin: float = 1.0) -> int:
+    """Function form of :func:`calibration` with the signature of the page's
+    ``calibrate_static_scales``: runs ``run_batches()`` under a calibration of ``layers``
+    and returns how many layers now have a static scale."""
+    with calibration(layers, margin) as calibrated:
+        run_batches()
+    return len(calibrated)

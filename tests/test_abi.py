@@ -120,3 +120,29 @@ def test_binding_raises_value_error():
     lib().nvfp4_linear(FAKE, 4, 24, FAKE, FAKE, FAKE, None, 8, None, 0, FAKE, FAKE, 1 << 20, None)
     with pytest.raises(ValueError, match="divisible by 16"):
         check(NVFP4_ERR_SHAPE)
+
+
+def test_misaligned_pointers_are_rejected():
+    # the header's alignment contract: codes and scales 8 bytes, out / bias 2, fp32 scalars 4
+    L = lib()
+    odd = ctypes.c_void_p(0x1004)
+    need = L.nvfp4_linear_workspace_bytes(4, 64, 8)
+    ws = ctypes.c_void_p(0x10000)
+    assert L.nvfp4_linear(FAKE, 4, 64, odd, FAKE, FAKE, None, 8, None, 0, FAKE, ws, need, None) == NVFP4_ERR_ARG
+    assert "packed must be 8-byte aligned" in _msg()
+    assert L.nvfp4_linear(FAKE, 4, 64, FAKE, odd, FAKE, None, 8, None, 0, FAKE, ws, need, None) == NVFP4_ERR_ARG
+    assert "inv_scale" in _msg()
+    assert L.nvfp4_linear(FAKE, 4, 64, FAKE, FAKE, FAKE, ctypes.c_void_p(0x1001), 8, None, 0, FAKE, ws, need,
+                          None) == NVFP4_ERR_ARG
+    assert "bias must be 2-byte aligned" in _msg()
+    assert L.nvfp4_linear(FAKE, 4, 64, FAKE, FAKE, ctypes.c_void_p(0x1002), None, 8, None, 0, FAKE, ws, need,
+                          None) == NVFP4_ERR_ARG
+    assert "global_sf_w must be 4-byte aligned" in _msg()
+    rc = L.nvfp4_gemm(FAKE, FAKE, 4, 64, FAKE, FAKE, 8, FAKE, FAKE, None, ctypes.c_void_p(0x1003), None, 0, None)
+    assert rc == NVFP4_ERR_ARG and "out must be 2-byte aligned" in _msg()
+    rc = L.nvfp4_gemm(FAKE, odd, 4, 64, FAKE, FAKE, 8, FAKE, FAKE, None, FAKE, None, 0, None)
+    assert rc == NVFP4_ERR_ARG and "x_scale" in _msg()
+    rc = L.nvfp4_quantize_activation(FAKE, 4, 64, None, 0, odd, FAKE, None, ws, 1 << 20, None)
+    assert rc == NVFP4_ERR_ARG and "codes must be 8-byte aligned" in _msg()
+    rc = L.nvfp4_quantize_weight(FAKE, 4, 64, FAKE, odd, FAKE, ws, 1 << 20, None)
+    assert rc == NVFP4_ERR_ARG and "inv_scale" in _msg()

@@ -132,7 +132,7 @@ def test_binding_rejects_bad_arguments():
         nv().nvfp4_linear(x[:, :200].contiguous(), packed[:, :100].contiguous(), inv_scale, gsf_w, None, lin.n)
     with pytest.raises(ValueError, match="rotation group"):
         nv().nvfp4_linear(x, packed, inv_scale, gsf_w, None, lin.n, rotation_group=12)
-    with pytest.raises(ValueError, match="act_scale"):
+    with pytest.raises(ValueError, match="activation-scale mode"):
         nv().NVFP4Linear(packed, inv_scale, gsf_w, None, lin.k, None, "bogus")
     with pytest.raises(ValueError):
         nv().NVFP4Linear.from_weight(torch.zeros((8, 24), device=DEV, dtype=torch.bfloat16))
@@ -362,3 +362,69 @@ def test_fp16_activation_decode_swiglu(m):
     two = nv().nvfp4_gemm(codes, scales, packed, inv_scale, used, gsf_w, None)
     torch.cuda.synchronize()
     assert torch.equal(out, two)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("which", ["qkv", "fc_in", "fc_out"])
+def test_segmented_vit_tiles_full_size(which):
+    """The ViT decoder batch at its configured size, in the call bench.py times: 8 tiles x
+    4096 tokens through nvfp4_linear_segmented with the group-16 rotation.  Every tile's
+    global scale is bit-exact against the oracle's (rotated amax of that tile alone); on
+    sampled rows of every tile the codes and scales of the segmented quantizer are
+    bit-exact and the outputs are within the GEMM tolerance of the oracle."""
+    lin = workloads.vit_decoder_tiles(tiles=8, which=(which,))[0]
+    g, rows, tiles = lin.rotation_group, lin.meta["tile_rows"], lin.meta["tiles"]
+    print(f"segmented full size: {which} {tiles} x [{rows}, {lin.k}] x [{lin.n}, {lin.k}] rot{g}", flush=True)
+    wd = nv().rotate_activation(lin.w.to(DEV).float(), g, out_dtype=torch.bfloat16)
+    packed, inv_scale, gsf_w = nv().quantize_weight(wd)
+    x = lin.x.to(DEV)
+    gsf_out = torch.empty((tiles,), dtype=torch.float32, device=DEV)
+    out = nv().nvfp4_linear_segmented(x, tiles, packed, inv_scale, gsf_w, None, lin.n, g, gsf_out=gsf_out)
+    codes, scales, gsf_q = nv().quantize_activation_segmented(x, tiles, g)
+    torch.cuda.synchronize()
+    assert torch.equal(gsf_out, gsf_q)
+    pw, sw, gw = o.quantize_weight(o.fold_weight(lin.w.float().numpy(), g))
+    assert np.array_equal(packed.cpu().numpy(), pw) and np.float32(gsf_w.item()) == gw
+    codes_c = codes.cpu().numpy()
+    scales_c = layout_to_canonical(scales.cpu().numpy(), tiles * rows, lin.k)
+    got = out.float().cpu().numpy()
+    xall = lin.x.float().numpy()
+    for t in range(tiles):
+        xt = o.rotate_activation(xall[t * rows:(t + 1) * rows], g)
+        gx = o.global_sf(o.amax(xt))
+        assert np.float32(gsf_out[t].item()) == gx, t
+        sample = np.arange(t % 7, rows, 257)
+        nib, s8 = o.nvfp4_quantize(xt[sample], gx)
+        assert np.array_equal(codes_c[t * rows + sample], o.pack_codes(nib)), t
+        assert np.array_equal(scales_c[t * rows + sample], s8), t
+        alpha = o.alpha_of(gx, gw)
+        ref = o.nvfp4_gemm(o.pack_codes(nib), s8, pw, sw, alpha)
+        bound = accumulation_bound(o.dequantize(o.pack_codes(nib), s8), o.dequantize(pw, sw), alpha)
+        assert_gemm_close(got[t * rows + sample], ref, bound)
+
+
+def test_calibration_block_and_errors():
+    """calibration(): inside the block the layer runs dynamic numerics and records; a block
+    that raises leaves the layer dynamic; a layer that saw no input is an error."""
+    lin = workloads.vit_decoder_tiles(tiles=2, tokens=128, which=("qkv",))[0]
+    g = lin.rotation_group
+    layer = nv().NVFP4Linear.from_weight(lin.w.to(DEV), None, rotation_group=g)
+    x = lin.x.to(DEV)
+    with nv().calibration([layer], margin=1.25):
+        assert layer.calibrating
+        inside = layer(x[:128])
+    assert not layer.calibrating and layer.act_scale == "static"
+    assert torch.equal(inside, nv().nvfp4_linear(x[:128], layer.packed, layer.inv_scale, layer.global_sf_w, None,
+                                                 lin.n, None, g))
+    rec = o.amax(o.rotate_activation(lin.x[:128].float().numpy(), g))
+    assert np.float32(layer.activation_global_sf().item()) == o.global_sf(np.float32(rec) * np.float32(1.25))
+    fresh = nv().NVFP4Linear.from_weight(lin.w.to(DEV), None, rotation_group=g)
+    with pytest.raises(KeyError):
+        with nv().calibration([fresh]):
+            fresh(x[:128])
+            raise KeyError("stop")
+    assert not fresh.calibrating and fresh.act_scale == "dynamic"
+    with pytest.raises(RuntimeError, match="no nonzero activation"):
+        with nv().calibration([fresh]):
+            pass
+    assert fresh.act_scale == "dynamic"
