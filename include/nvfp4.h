@@ -61,6 +61,7 @@ enum { NVFP4_DTYPE_BF16 = 0, NVFP4_DTYPE_F32 = 1 };
 #define NVFP4_SCALE_TILE_K 128
 #define NVFP4_MAX_ROTATION_GROUP 128
 #define NVFP4_WORKSPACE_ALIGN 256
+#define NVFP4_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)   /* nvfp4_linear_noalloc's fixed device scratch */
 
 /* Alignment.  Every call checks its pointers and returns NVFP4_ERR_ARG for a misaligned
  * one, before anything is queued:
@@ -200,6 +201,30 @@ int nvfp4_linear(const void* x_dev, int64_t m, int64_t k,
                  const float* global_sf_w_dev, const void* bias_dev, int64_t out_features,
                  const float* global_sf_x_dev, int rotation_group, void* out_dev,
                  void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/*
+ * nvfp4_linear_noalloc: nvfp4_linear for callers that cannot allocate memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments without the workspace, the same result.  Instead of a caller workspace it
+ * uses a fixed device array of NVFP4_NOALLOC_SCRATCH_BYTES that the library holds on
+ * every device it runs on until the process ends; the call itself allocates nothing.
+ *   - Size limit: the call succeeds when the nvfp4_linear workspace without its split-K
+ *     region fits (activation codes m*k/2 and scales nvfp4_scale_bytes(m, k), plus
+ *     64 KiB, plus 2*m*k bytes when m <= 4; about m*k <= 119 M values).  When
+ *     nvfp4_linear_workspace_bytes(m, k, out_features) itself fits, the output is
+ *     bit-identical to nvfp4_linear's; otherwise the GEMM's last round of tiles runs
+ *     unsplit (the same function, fp32 summation order aside).  Larger inputs return
+ *     NVFP4_ERR_WORKSPACE before anything is queued.
+ *   - Every call on a device shares that device's array, and nothing in it needs to
+ *     start at zero (each call writes what it reads).  Calls that overlap on one device
+ *     (other streams, other threads) race on it: serialise them.
+ *   - The first call on a device looks the array's address up (no allocation); make it
+ *     outside graph capture.
+ */
+int nvfp4_linear_noalloc(const void* x_dev, int64_t m, int64_t k,
+                         const uint8_t* packed_dev, const uint8_t* inv_scale_dev,
+                         const float* global_sf_w_dev, const void* bias_dev, int64_t out_features,
+                         const float* global_sf_x_dev, int rotation_group, void* out_dev, void* stream);
 
 /*
  * nvfp4_linear_segmented: `segments` tiles of seg_rows rows through one linear in one

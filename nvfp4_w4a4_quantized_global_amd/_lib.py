@@ -19,6 +19,7 @@ NVFP4_ERR_WORKSPACE = -3
 NVFP4_ERR_HIP = -4
 NVFP4_DTYPE_BF16 = 0
 NVFP4_DTYPE_F32 = 1
+NVFP4_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -46,6 +47,7 @@ SIGNATURES = {
     "nvfp4_quantize_activation_segmented": (_int, [_vp, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_gemm": (_int, [_vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_linear": (_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _int, _vp, _vp, _sz, _vp]),
+    "nvfp4_linear_noalloc": (_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _int, _vp, _vp]),
     "nvfp4_linear_segmented": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _int, _vp, _vp, _vp, _sz,
                                       _vp]),
     "nvfp4_scale_to_canonical": (_int, [_vp, _vp, _i64, _i64, _vp]),

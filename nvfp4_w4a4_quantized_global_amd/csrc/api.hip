@@ -9,6 +9,8 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "../../include/nvfp4.h"
 #include "nvfp4_launch.h"
 
@@ -211,6 +213,34 @@ int linear_impl(const char* fn, const void* x, int64_t segments, int64_t seg_row
                                        per_segment ? seg_rows : 0, static_cast<const uint16_t*>(bias),
                                        static_cast<uint16_t*>(out), ws.gemm, ws.gemm_bytes, s),
                     fn);
+}
+
+// Fixed device scratch of nvfp4_linear_noalloc, for callers that cannot allocate.
+// Each device the library runs on holds its own copy until the process ends.  In host
+// code `scratch` names a host-side stand-in, never the device memory: its device
+// address is resolved once per device with hipGetSymbolAddress and only that address
+// is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[NVFP4_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// The current device's scratch address, resolved on the first call on that device.
+int scratch_of_current_device(const char* fn, void** ptr) {
+  int dev = -1;
+  if (int rc = hip_status(hipGetDevice(&dev), fn)) return rc;
+  if (dev < 0 || dev >= kMaxDevices) return fail(NVFP4_ERR_HIP, "%s: device %d beyond the %d supported", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    if (int rc = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), fn)) return rc;
+    if (p == nullptr || (uintptr_t)p % NVFP4_WORKSPACE_ALIGN)
+      return fail(NVFP4_ERR_HIP, "%s: scratch of device %d resolved to an unusable address", fn, dev);
+    g_scratch_dev[dev] = p;
+  }
+  *ptr = g_scratch_dev[dev];
+  return NVFP4_OK;
 }
 
 }  // namespace
@@ -460,6 +490,30 @@ int nvfp4_linear(const void* x, int64_t m, int64_t k, const uint8_t* packed, con
   g_err[0] = 0;
   return linear_impl("nvfp4_linear", x, 1, m, k, packed, inv_scale, global_sf_w, bias, out_features, global_sf_x,
                      rotation_group, out, nullptr, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+int nvfp4_linear_noalloc(const void* x, int64_t m, int64_t k, const uint8_t* packed, const uint8_t* inv_scale,
+                         const float* global_sf_w, const void* bias, int64_t out_features, const float* global_sf_x,
+                         int rotation_group, void* out, void* stream) {
+  const char* fn = "nvfp4_linear_noalloc";
+  g_err[0] = 0;
+  if (int rc = check_rows_k(fn, m, k, true)) return rc;
+  if (out_features <= 0 || out_features >= kMaxDim)
+    return fail(NVFP4_ERR_SHAPE, "%s: out_features must be in [1, 2^31), got %lld", fn, (long long)out_features);
+  if (m == 0) return NVFP4_OK;
+  // the whole nvfp4_linear workspace when it fits, else the one without split-K partials
+  const bool split_k = carve(nullptr, m, k, out_features).bytes <= NVFP4_NOALLOC_SCRATCH_BYTES;
+  const size_t need = carve(nullptr, m, k, out_features, 1, split_k).bytes;
+  if (need > NVFP4_NOALLOC_SCRATCH_BYTES)
+    return fail(NVFP4_ERR_WORKSPACE,
+                "%s: an [%lld, %lld] input needs %zu bytes of scratch, more than the fixed %zu; call nvfp4_linear "
+                "with a workspace instead",
+                fn, (long long)m, (long long)k, need, (size_t)NVFP4_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (int rc = scratch_of_current_device(fn, &ws)) return rc;
+  return linear_impl(fn, x, 1, m, k, packed, inv_scale, global_sf_w, bias, out_features, global_sf_x, rotation_group,
+                     out, nullptr, ws, NVFP4_NOALLOC_SCRATCH_BYTES, static_cast<hipStream_t>(stream), nullptr,
+                     split_k);
 }
 
 int nvfp4_linear_segmented(const void* x, int64_t segments, int64_t seg_rows, int64_t k, const uint8_t* packed,

@@ -205,6 +205,42 @@ def nvfp4_linear(x: torch.Tensor, packed: torch.Tensor, inv_scale: torch.Tensor,
     return out.reshape(*orig[:-1], out_features)
 
 
+def nvfp4_linear_noalloc(x: torch.Tensor, packed: torch.Tensor, inv_scale: torch.Tensor, global_sf_w: torch.Tensor,
+                         bias: torch.Tensor | None, out_features: int, global_sf_x=None, rotation_group: int = 0,
+                         out: torch.Tensor | None = None) -> torch.Tensor:
+    """:func:`nvfp4_linear` through the library's allocation-free entry point: its scratch
+    is a fixed device array of the library, so the call needs no workspace.  Pass
+    ``out`` (and a device-tensor ``global_sf_x``) to keep this wrapper from allocating
+    too.  Calls that overlap on one device race on that array."""
+    if x.dtype != torch.bfloat16:
+        raise ValueError(f"x must be bf16, got {x.dtype}")
+    orig = x.shape
+    k = orig[-1]
+    x2d = x.reshape(-1, k)
+    _require_cuda("x", x2d, torch.bfloat16, 2)
+    _require_cuda("packed", packed, torch.uint8, 2)
+    if packed.shape[0] != out_features or packed.shape[1] * 2 != k:
+        raise ValueError(f"packed NVFP4 weight must be uint8 [{out_features}, {k // 2}], got "
+                         f"{packed.dtype} {list(packed.shape)}")
+    _require_cuda("inv_scale", inv_scale, torch.uint8)
+    if inv_scale.numel() < scale_bytes(out_features, k):
+        raise ValueError("inv_scale is smaller than nvfp4_scale_bytes(out_features, K)")
+    gw = _scalar_f32(global_sf_w, x.device)
+    gx = None if global_sf_x is None else _scalar_f32(global_sf_x, x.device)
+    if bias is not None:
+        _require_cuda("bias", bias, torch.bfloat16)
+        if bias.numel() != out_features:
+            raise ValueError(f"bias must have {out_features} elements, got {bias.numel()}")
+    m = x2d.shape[0]
+    if out is None:
+        out = torch.empty((m, out_features), dtype=torch.bfloat16, device=x.device)
+    elif out.shape != (m, out_features) or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous bf16 [{m}, {out_features}] tensor")
+    check(lib().nvfp4_linear_noalloc(_ptr(x2d), m, k, _ptr(packed), _ptr(inv_scale), _ptr(gw), _ptr(bias),
+                                     out_features, _ptr(gx), int(rotation_group), _ptr(out), _stream(x.device)))
+    return out.reshape(*orig[:-1], out_features)
+
+
 def amax(x: torch.Tensor, rotation_group: int = 0, out: torch.Tensor | None = None,
          accumulate: bool = False) -> torch.Tensor:
     """max |x| over a bf16 [.., K] input after the optional block rotation, as an fp32 0-d
