@@ -70,6 +70,7 @@ __all__ = [
     "sylvester_hadamard", "fwht_f32", "rotate_activation", "fold_weight", "amax", "global_sf",
     "nvfp4_quantize", "pack_codes", "unpack_codes", "dequantize", "dequantize_values", "quantize_weight",
     "alpha_of", "nvfp4_gemm", "nvfp4_linear_inference", "probe_relative_error", "exp_f32", "swiglu_product",
+    "ste_linear_grads",
 ]
 
 # ---------------------------------------------------------------------------
@@ -388,3 +389,42 @@ def probe_relative_error(out_values: np.ndarray, x_bf16_values: np.ndarray, w_bf
     ref = np.asarray(x_bf16_values, dtype=np.float64) @ np.asarray(w_bf16_values, dtype=np.float64).T
     diff = np.asarray(out_values, dtype=np.float64) - ref
     return float(np.linalg.norm(diff) / max(np.linalg.norm(ref), 1e-12))
+
+
+# ---------------------------------------------------------------------------
+# Training: the straight-through estimator.  [DEC] module docstring: training runs
+# through _NVFP4DecoderSTE, whose forward is the inference function and whose backward
+# is full precision; NVFP4DecoderLinear.forward rotates the activation before the STE
+# (the weight parameter is the already rotated master).  The backward is therefore the
+# gradient of the full-precision linear y = x_r W^T + b with x_r = rotate(x), the
+# quantization taken as the identity, chained through the rotation.
+# ---------------------------------------------------------------------------
+def ste_linear_grads(grad_out, x_values, w_master, rotation_group: int = 0, with_bias: bool = True) -> dict:
+    """float64 gradients of the STE linear for an upstream gradient ``grad_out [M, N]``:
+    ``x`` [M, K] (the layer input, bf16 values), ``w`` [N, K] (the master weight,
+    rotated along K when the layer rotates).  Returns ``grad_x`` [M, K], ``grad_w``
+    [N, K] and, with a bias, ``grad_b`` [N].  The weight gradient uses the rotated input
+    the layer computes with, ``rotate_activation(x)`` rounded to bf16 ([DEC]
+    NVFP4DecoderLinear.forward rotates in the compute dtype before the STE); the
+    rotation's own gradient is its transpose, which for the scaled Sylvester matrix is
+    itself, applied exactly."""
+    gy = np.asarray(grad_out, dtype=np.float64)
+    x = np.asarray(x_values, dtype=np.float64)
+    w = np.asarray(w_master, dtype=np.float64)
+    if rotation_group:
+        g = rotation_group
+        r = sylvester_hadamard(g).astype(np.float64) / math.sqrt(g)
+        x_r = rotate_activation(x.astype(np.float32), g, out="bf16").astype(np.float64)
+    else:
+        r = None
+        x_r = x
+    grad_xr = gy @ w
+    if r is not None:
+        rows, k = grad_xr.shape
+        grad_x = (grad_xr.reshape(rows, k // g, g) @ r.T).reshape(rows, k)
+    else:
+        grad_x = grad_xr
+    out = {"grad_x": grad_x, "grad_w": gy.T @ x_r}
+    if with_bias:
+        out["grad_b"] = gy.sum(axis=0)
+    return out
