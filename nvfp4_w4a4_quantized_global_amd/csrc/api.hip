@@ -133,6 +133,9 @@ int quantize_impl(const char* fn, const void* x, int64_t m, int64_t k, const flo
   const int64_t seg_rows = m / segments;
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   const uint16_t* upp = static_cast<const uint16_t*>(up);
+  if (gsf_static == nullptr && segments == 1 && up == nullptr &&
+      nvfp4::quantize_small_supported(m, k))   // small input: both passes in one launch
+    return hip_status(nvfp4::launch_quantize_small(xp, m, k, group, c, codes, scales, gsf_out, s, a16), fn);
   if (gsf_static == nullptr) {
     uint16_t* xout = upp != nullptr ? static_cast<uint16_t*>(xbuf) : nullptr;
     int rc = hip_status(nvfp4::launch_amax_partials(xp, upp, xout, seg_rows, k, (int)segments, group, c, partials,

@@ -10,7 +10,7 @@ namespace nvfp4 {
 
 // Upper bound on the number of per-block partial maxima of the amax pass, and on the
 // number of segments (row blocks with their own scale) of one call.
-constexpr int kMaxAmaxPartials = 4096;
+constexpr int kMaxAmaxPartials = 8192;
 constexpr int kMaxSegments = 1024;
 
 // Partial maxima of `segments` consecutive row blocks of seg_rows rows each (one
@@ -30,6 +30,14 @@ hipError_t launch_quantize(const uint16_t* x, const uint16_t* up, int64_t rows, 
                            float inv_sqrt_g, const float* static_gsf, const float* partials, int n_partials,
                            int64_t seg_rows, int segments, uint8_t* codes, uint8_t* scales, float* gsf_out,
                            hipStream_t s, uint16_t* a16 = nullptr);
+
+// Dynamic-scale quantize of a small input (rows * k within quantize_small_supported) in
+// one launch: the same codes, scales, global scale (*gsf_out) and a16 as
+// launch_amax_partials followed by launch_quantize with one segment.
+bool quantize_small_supported(int64_t rows, int64_t k);
+hipError_t launch_quantize_small(const uint16_t* x, int64_t rows, int64_t k, int group, float inv_sqrt_g,
+                                 uint8_t* codes, uint8_t* scales, float* gsf_out, hipStream_t s,
+                                 uint16_t* a16 = nullptr);
 
 // x [rows][k] = bf16 SwiGLU product of gate and up.
 hipError_t launch_swiglu(const uint16_t* gate, const uint16_t* up, uint16_t* x, int64_t rows, int64_t k, hipStream_t s);

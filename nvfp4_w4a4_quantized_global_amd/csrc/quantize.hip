@@ -20,8 +20,24 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kAmaxBlocks = 512;   // partial maxima of the amax pass (<= kMaxAmaxPartials)
-static_assert(8 * kAmaxBlocks <= kMaxAmaxPartials, "partials buffer");
+// Launch shapes of the two passes.  Each can be set at build time (-D) for tuning sweeps.
+#ifndef NVFP4_AMAX_BLOCKS
+#define NVFP4_AMAX_BLOCKS 512
+#endif
+#ifndef NVFP4_AMAX_UNROLL
+#define NVFP4_AMAX_UNROLL 4
+#endif
+#ifndef NVFP4_QUANT_UNITS
+#define NVFP4_QUANT_UNITS 2
+#endif
+#ifndef NVFP4_QUANT_BLOCKS
+#define NVFP4_QUANT_BLOCKS 2048
+#endif
+#ifndef NVFP4_SMALL_QUANT_VALUES
+#define NVFP4_SMALL_QUANT_VALUES 65536
+#endif
+constexpr int kAmaxBlocks = NVFP4_AMAX_BLOCKS;   // partial maxima of the amax pass (<= kMaxAmaxPartials)
+static_assert(4 * kAmaxBlocks <= kMaxAmaxPartials, "partials buffer");   // SwiGLU: 4x the grid
 
 struct Chunk16 {
   float v[16];
@@ -53,7 +69,7 @@ __device__ __forceinline__ float block_max(float x, float* lds) {
 // consecutive 16-value chunks, so the lanes holding one rotation group are
 // consecutive and aligned (the group divides the row length); each lane keeps
 // kAmaxUnroll chunks in flight.
-constexpr int kAmaxUnroll = 4;
+constexpr int kAmaxUnroll = NVFP4_AMAX_UNROLL;
 
 // Stores 16 values that are already bf16-exact as bf16.
 __device__ __forceinline__ void store16_bf16(uint16_t* __restrict__ p, const float (&v)[16]) {
@@ -122,17 +138,51 @@ __global__ void __launch_bounds__(kThreads) amax_partial_kernel(const uint16_t* 
   if (threadIdx.x == 0) partials[blockIdx.y * gridDim.x + blockIdx.x] = m;
 }
 
+// One lane's share of a quantize unit (row, 128-wide K tile): lane j of the unit's eight
+// owns 16-block j.  v holds its 16 input values (zeros past the end); the block is
+// rotated (all lanes of the wave take part), quantized under global scale gsf, and its
+// codes (and, with a16, its fp16 operand form) stored; the unit's 8 scale bytes are
+// gathered into lane j == 0 and written as one 8-byte word.
+template <bool kRotate>
+__device__ __forceinline__ void quantize_unit(float (&v)[16], int64_t row, int64_t kt, int j, int64_t m_rows,
+                                              int64_t k, int group, float inv_sqrt_g, float gsf,
+                                              uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                              uint16_t* __restrict__ a16) {
+  if (kRotate) rotate16_bf16(v, group, inv_sqrt_g);
+  const int64_t blk = kt * 8 + j;
+  const bool in_row = row < m_rows;
+  const bool valid = in_row && blk < k / kBlock;
+  uint32_t w0, w1;
+  const uint32_t s8 = quantize_block16(v, gsf, valid, w0, w1);
+  if (valid) *reinterpret_cast<uint2*>(codes + row * (k / 2) + blk * 8) = make_uint2(w0, w1);
+  if (a16 != nullptr && valid) {
+    // the block's values in the GEMMs' operand form: fp16 code * scale * 2^-8, exact
+    const gemm::half2_t sc = gemm::as_half2((s8 << 7) | (s8 << 23));
+    uint4* d = reinterpret_cast<uint4*>(a16 + row * k + blk * kBlock);
+    d[0] = __builtin_bit_cast(uint4, gemm::dequant8(w0, sc));
+    d[1] = __builtin_bit_cast(uint4, gemm::dequant8(w1, sc));
+  }
+  uint32_t lo = j < 4 ? s8 << (8 * j) : 0u;
+  uint32_t hi = j >= 4 ? s8 << (8 * (j - 4)) : 0u;
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) {
+    lo |= __shfl_xor(lo, o, 64);
+    hi |= __shfl_xor(hi, o, 64);
+  }
+  if (j == 0 && in_row) *reinterpret_cast<uint2*>(scales + (kt * m_rows + row) * 8) = make_uint2(lo, hi);
+}
+
 // Pass 2: quantize.  Eight consecutive lanes own one 128-wide K tile of one row
 // (a "unit"; lane j of the eight owns the 16-block j of the tile), so each group of
 // eight reads 256 contiguous bytes and writes 64 contiguous code bytes and the 8
 // scale bytes that are contiguous in the k-tile-major scale layout.  Blocks take the
 // global scale once, then loop over groups of kQuantUnits x 32 units, loading a
 // group's units before computing them.
-constexpr int kQuantUnits = 2;
+constexpr int kQuantUnits = NVFP4_QUANT_UNITS;
 // Grid cap (blocks loop over the units): more blocks in flight pay off once the input
 // is several times larger than one pass of the cap; below that the per-block scale
 // prologue dominates.
-constexpr int kQuantBlocks = 2048;
+constexpr int kQuantBlocks = NVFP4_QUANT_BLOCKS;
 constexpr int kQuantBlocksLarge = 8192;
 constexpr int64_t kLargeUnits = (int64_t)1 << 19;
 
@@ -200,31 +250,68 @@ __global__ void __launch_bounds__(kThreads) quantize_kernel(
 
 #pragma unroll
     for (int u = 0; u < kQuantUnits; ++u) {
-      if (kRotate) rotate16_bf16(v[u], group, inv_sqrt_g);
-      const int64_t blk = kt[u] * 8 + j;
       const bool in_row = row[u] < m_rows;
-      const bool valid = in_row && blk < nb;
       const float gsf = dynamic ? __uint_as_float(seg_amax[in_row ? row[u] / seg_rows : 0]) : gsf_static;
-      uint32_t w0, w1;
-      const uint32_t s8 = quantize_block16(v[u], gsf, valid, w0, w1);
-      if (valid) *reinterpret_cast<uint2*>(codes + row[u] * (k / 2) + blk * 8) = make_uint2(w0, w1);
-      if (a16 != nullptr && valid) {
-        // the block's values in the GEMMs' operand form: fp16 code * scale * 2^-8, exact
-        const gemm::half2_t sc = gemm::as_half2((s8 << 7) | (s8 << 23));
-        uint4* d = reinterpret_cast<uint4*>(a16 + row[u] * k + blk * kBlock);
-        d[0] = __builtin_bit_cast(uint4, gemm::dequant8(w0, sc));
-        d[1] = __builtin_bit_cast(uint4, gemm::dequant8(w1, sc));
-      }
-      // gather the unit's 8 scale bytes into lane j == 0 and write them as one 8-byte word
-      uint32_t lo = j < 4 ? s8 << (8 * j) : 0u;
-      uint32_t hi = j >= 4 ? s8 << (8 * (j - 4)) : 0u;
-#pragma unroll
-      for (int o = 1; o < 8; o <<= 1) {
-        lo |= __shfl_xor(lo, o, 64);
-        hi |= __shfl_xor(hi, o, 64);
-      }
-      if (j == 0 && in_row) *reinterpret_cast<uint2*>(scales + (kt[u] * m_rows + row[u]) * 8) = make_uint2(lo, hi);
+      quantize_unit<kRotate>(v[u], row[u], kt[u], j, m_rows, k, group, inv_sqrt_g, gsf, codes, scales, a16);
     }
+  }
+}
+
+// Dynamic-scale quantize of a small input in one launch: one workgroup computes the
+// abs-max of the whole (rotated) input, forms the global scale and quantizes, so the
+// two passes above cost one launch instead of two.  For inputs of at most
+// kSmallQuantValues values, where launch and ramp time outweigh the streaming.
+constexpr int kSmallThreads = 1024;
+constexpr int64_t kSmallQuantValues = NVFP4_SMALL_QUANT_VALUES;
+
+template <bool kRotate>
+__global__ void __launch_bounds__(kSmallThreads) quantize_small_kernel(
+    const uint16_t* __restrict__ x, int64_t m_rows, int64_t k, int group, float inv_sqrt_g,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gsf_out,
+    uint16_t* __restrict__ a16) {
+  __shared__ float lds[kSmallThreads / 64];
+  const int t = threadIdx.x;
+  // pass 1: consecutive lanes take consecutive 16-value chunks (a rotation group's
+  // chunks sit in consecutive, aligned lanes)
+  const int64_t n_chunks = m_rows * k / kBlock;
+  float mx = 0.0f;
+  for (int64_t c0 = 0; c0 < n_chunks; c0 += kSmallThreads) {
+    const int64_t c = c0 + t;
+    float v[16];
+    if (c < n_chunks) {
+      load16_bf16(x + c * kBlock, v);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = 0.0f;
+    }
+    if (kRotate) rotate16_bf16(v, group, inv_sqrt_g);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(v[i]));
+  }
+  mx = wave_max(mx);
+  if ((t & 63) == 0) lds[t >> 6] = mx;
+  __syncthreads();
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kSmallThreads / 64; ++i) amax = fmaxf(amax, lds[i]);
+  const float gsf = global_scale_from_amax(amax);
+  if (t == 0 && gsf_out != nullptr) *gsf_out = gsf;
+  // pass 2: the units of quantize_kernel, eight lanes each (the input is re-read from L2)
+  const int64_t kt_count = (k + kScaleTileK - 1) / kScaleTileK;
+  const int64_t units = m_rows * kt_count;
+  const int j = t & 7;
+  for (int64_t u0 = 0; u0 < units; u0 += kSmallThreads / 8) {
+    const int64_t unit = u0 + (t >> 3);
+    const int64_t row = unit / kt_count, kt = unit - row * kt_count;
+    const int64_t blk = kt * 8 + j;
+    float v[16];
+    if (row < m_rows && blk < k / kBlock) {
+      load16_bf16(x + row * k + blk * kBlock, v);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = 0.0f;
+    }
+    quantize_unit<kRotate>(v, row, kt, j, m_rows, k, group, inv_sqrt_g, gsf, codes, scales, a16);
   }
 }
 
@@ -391,6 +478,19 @@ hipError_t launch_quantize(const uint16_t* x, const uint16_t* up, int64_t rows, 
   else
     hipLaunchKernelGGL((quantize_kernel<false, false>), g1, dim3(kThreads), 0, s, x, up, rows, k, group, inv_sqrt_g,
                        static_gsf, partials, n_partials, seg_rows, segments, codes, scales, gsf_out, a16);
+  return hipGetLastError();
+}
+
+bool quantize_small_supported(int64_t rows, int64_t k) { return rows * k <= kSmallQuantValues; }
+
+hipError_t launch_quantize_small(const uint16_t* x, int64_t rows, int64_t k, int group, float inv_sqrt_g,
+                                 uint8_t* codes, uint8_t* scales, float* gsf_out, hipStream_t s, uint16_t* a16) {
+  if (group > 1)
+    hipLaunchKernelGGL(quantize_small_kernel<true>, dim3(1), dim3(kSmallThreads), 0, s, x, rows, k, group, inv_sqrt_g,
+                       codes, scales, gsf_out, a16);
+  else
+    hipLaunchKernelGGL(quantize_small_kernel<false>, dim3(1), dim3(kSmallThreads), 0, s, x, rows, k, group,
+                       inv_sqrt_g, codes, scales, gsf_out, a16);
   return hipGetLastError();
 }
 
