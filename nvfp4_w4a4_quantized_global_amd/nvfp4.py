@@ -442,6 +442,66 @@ def scale_from_canonical(canonical: torch.Tensor) -> torch.Tensor:
     return out[: scale_bytes(rows, k)]
 
 
+class _NVFP4STEFn(torch.autograd.Function):
+    """Straight-through NVFP4 linear ("minimax_h3_nvfp4_decoder": the training path's
+    _NVFP4DecoderSTE, forward = the inference function, backward = full precision; the
+    layer rotates its input first).
+
+    Forward: the master weight is packed afresh (it changes every optimizer step) and
+    the library's nvfp4_linear runs on the bf16 input with its rotation fused into the
+    quantizer (bit-identical to rotating first).  Backward: the gradient of the
+    full-precision linear on the rotated input, the quantization taken as the identity:
+    grad_x = rotate(grad_y W) (the scaled Sylvester block is symmetric and orthonormal,
+    so the rotation is its own transpose), grad_W = grad_y^T rotate(x), grad_b = sum of
+    grad_y over rows; the products accumulate in fp32 and grad_x is rounded to bf16 once,
+    after its rotation.  The two products are plain library GEMMs (hipBLASLt through
+    torch.matmul): the backward is not part of the inference path."""
+
+    @staticmethod
+    def forward(ctx, x: torch.Tensor, weight: torch.Tensor, bias, global_sf_x, group: int):
+        packed, inv_scale, gsf_w = quantize_weight(weight.detach().to(torch.bfloat16).contiguous())
+        b = None if bias is None else bias.detach().to(torch.bfloat16).contiguous()
+        ctx.save_for_backward(x, weight)
+        ctx.group = group
+        ctx.has_bias = bias is not None
+        ctx.bias_dtype = None if bias is None else bias.dtype
+        return nvfp4_linear(x, packed, inv_scale, gsf_w, b, weight.shape[0], global_sf_x, group)
+
+    @staticmethod
+    def backward(ctx, grad_y: torch.Tensor):
+        x, weight = ctx.saved_tensors
+        n, k = weight.shape
+        g = ctx.group
+        gy = grad_y.reshape(-1, n).float()
+        grad_x = grad_w = grad_b = None
+        if ctx.needs_input_grad[0]:
+            gxr = gy @ weight.float()
+            grad_x = (rotate_activation(gxr.contiguous(), g, out_dtype=x.dtype) if g else gxr.to(x.dtype))
+            grad_x = grad_x.reshape(x.shape)
+        if ctx.needs_input_grad[1]:
+            x2 = x.reshape(-1, k)
+            xr = rotate_activation(x2.contiguous(), g) if g else x2
+            grad_w = (gy.t() @ xr.float()).to(weight.dtype)
+        if ctx.has_bias and ctx.needs_input_grad[2]:
+            grad_b = gy.sum(0).to(ctx.bias_dtype)
+        return grad_x, grad_w, grad_b, None, None
+
+
+def nvfp4_linear_train(x: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor | None = None, global_sf_x=None,
+                       rotation_group: int = 0) -> torch.Tensor:
+    """Differentiable NVFP4 linear for training (straight-through estimator).
+
+    ``weight`` is the full-precision master [out, in] (already rotated along ``in`` when
+    ``rotation_group`` is set, as from_weight's fold leaves it); ``x`` is cast to bf16.
+    The forward equals :func:`nvfp4_linear` on the packed master weight; gradients flow
+    to ``x``, ``weight`` and ``bias`` as through the full-precision linear."""
+    x = x.to(torch.bfloat16)
+    if x.dim() < 1 or not x.is_contiguous():
+        x = x.contiguous()
+    gx = None if global_sf_x is None else _scalar_f32(global_sf_x, x.device)
+    return _NVFP4STEFn.apply(x, weight, bias, gx, int(rotation_group or 0))
+
+
 def _check_layer_geometry(packed: torch.Tensor, in_features: int, rotation_group: int | None) -> None:
     """A packed NVFP4 weight must hold whole 16-value blocks of every row, and a rotation
     group must tile the input dimension exactly."""
