@@ -54,8 +54,10 @@ def parse():
     p.add_argument("--cpu-rows", type=int, default=M, help="rows of the CPU oracle sample")
     p.add_argument("--cpu-repeats", type=int, default=4,
                    help="times the oracle runs the sample (the rate is the total work over the total time)")
-    p.add_argument("--part", choices=("step", "gemm", "quantize", "copy"),
-                   help="run only this part (warmup + steps launches, no JSON line): for counter runs")
+    p.add_argument("--part", choices=("step", "gemm", "quantize", "copy", "decode"),
+                   help="run only this part (warmup + steps launches, no JSON line): for counter runs; "
+                        "decode = the gate projection at one row: nvfp4_gemm, the static nvfp4_linear and a "
+                        "plain torch read of the same weight bytes, each over 4 weight copies in turn")
     p.add_argument("--decode", action="store_true",
                    help="time the decode shapes instead (M = 1, 16 and 128 on the 7 projections; one line per "
                         "shape, no JSON line)")
@@ -423,6 +425,39 @@ def graph_time_us(fns, reps: int) -> float:
     return a.elapsed_time(b) / (reps * len(fns)) * 1e3
 
 
+def decode_part(nv, workloads, dev, calls: int) -> None:
+    """Counter-run workload for the decode kernels: the gate projection at one row, 4
+    weight copies in turn (so the weight comes from HBM).  In order: `calls` calls of
+    nvfp4_gemm (gemm_decode_kernel on activation codes), of the static-scale nvfp4_linear
+    (gemm_decode_kernel on the fp16 activation), and of a plain read of the packed weight
+    bytes (torch's amax over them as int32: the same bytes, no NVFP4 work)."""
+    import torch
+    w = workloads.small_m_weight("mlp.gate_proj").to(dev)
+    n, k = w.shape
+    packed, inv_scale, gsf_w = nv.quantize_weight(w)
+    del w
+    copies = [(packed.clone(), inv_scale.clone()) for _ in range(DECODE_COPIES)]
+    x = workloads.small_m_input(1, "mlp.gate_proj").to(dev)
+    gx = nv.static_global_sf(nv.amax(x), 1.0)
+    codes, scales, _ = nv.quantize_activation(x, gx)
+    out = torch.empty((1, n), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty((nv.linear_workspace_bytes(1, k, n),), dtype=torch.uint8, device=dev)
+    gws = torch.empty((max(nv.gemm_workspace_bytes(1, k, n), 256),), dtype=torch.uint8, device=dev)
+    red = torch.empty((), dtype=torch.int32, device=dev)
+    for i in range(calls):
+        p, sc = copies[i % DECODE_COPIES]
+        nv.nvfp4_gemm(codes, scales, p, sc, gx, gsf_w, None, out, gws)
+    torch.cuda.synchronize()
+    for i in range(calls):
+        p, sc = copies[i % DECODE_COPIES]
+        nv.nvfp4_linear(x, p, sc, gsf_w, None, n, gx, 0, ws, out)
+    torch.cuda.synchronize()
+    for i in range(calls):
+        torch.amax(copies[i % DECODE_COPIES][0].view(torch.int32).view(-1), dim=0, out=red)
+    torch.cuda.synchronize()
+    print(f"decode: 3 x {calls} calls", flush=True)
+
+
 def decode_table(nv, workloads, dev) -> None:
     """The decode sweep (C5): x N(0,1), W N(0,0.02), M in {1, 16, 128} on the 7
     projections; static scale = the one calibrated on x itself (margin 1).  Columns: the
@@ -598,6 +633,9 @@ def main():
         return
     if args.tables:
         other_tables(nv, workloads, dev, Clock(torch, dev))
+        return
+    if args.part == "decode":
+        decode_part(nv, workloads, dev, args.warmup + args.steps)
         return
     if args.part == "copy":
         # two plain copies of 1 GiB: the runtime's copy kernel, and torch's vectorised

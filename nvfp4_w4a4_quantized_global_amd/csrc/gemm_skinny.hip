@@ -265,8 +265,8 @@ int skinny_splits(int64_t k, int64_t n, int cus) {
 }
 
 // Decode (m <= 16): a block owns 16 weight rows (one MFMA column tile) and a K range
-// whose 256-wide super tiles its four waves split into four consecutive quarters.  Each
-// wave streams its quarter through a ring of kDecDepth LDS slots with direct
+// whose 256-wide super tiles its waves (four or eight) split into consecutive ranges.
+// Each wave streams its range through a ring of kDecDepth LDS slots with direct
 // global -> LDS loads (global_load_lds), one slot per super tile: the 16 weight rows and
 // the m (<= 16, clamped) activation rows as whole 128-byte lines (load instruction h
 // covers rows 8h .. 8h + 7, lane l: row 8h + l / 8, 16-byte position l % 8), and the
@@ -295,12 +295,12 @@ __device__ __forceinline__ void dec_dma16(const uint8_t* src, uint8_t* dst) {
 __device__ __forceinline__ void dec_dma4(const uint8_t* src, uint8_t* dst) {
   asm volatile("global_load_lds_dword %1, off" :: "{m0}"((uint32_t)(uintptr_t)dst), "v"(src) : "memory");
 }
-// Waits until at most one super tile's kLoads direct loads (the newer one) are in
+// Waits until at most one super tile's kCount direct loads (the newer one) are in
 // flight; the compiler moves no memory access across it.
-template <int kLoads>
-__device__ __forceinline__ void dec_wait_one_behind() {
-  static_assert(kDecDepth == 2 && (kLoads == 5 || kLoads == 6), "wait count");
-  if constexpr (kLoads == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+template <int kCount>
+__device__ __forceinline__ void dec_wait() {
+  static_assert(kDecDepth == 2 && (kCount == 5 || kCount == 6), "wait count");
+  if constexpr (kCount == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
 }
 __device__ __forceinline__ void dec_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -312,16 +312,23 @@ __device__ __forceinline__ void dec_lds_order() { asm volatile("s_waitcnt lgkmcn
 // that read one chunk of rows l16 % 4 hit four distinct bank groups), and the kernel
 // expands only the weight.  MFMA rows 4 .. 15 multiply rows l16 % 4 again, into output
 // rows that are never written.
-template <bool kA16>
-__global__ void __launch_bounds__(256) gemm_decode_kernel(
+//
+// kDW: waves per block (4 or 8).  Eight waves split the block's K range eight ways, which
+// takes the place of a two-way block-level K split: the partial sums meet in LDS and the
+// second launch (gemm_skinny_reduce) is not needed.
+//
+// Four waves per SIMD (two eight-wave or four four-wave blocks per compute unit, as the
+// LDS allows) bound the registers.
+template <bool kA16, int kDW>
+__global__ void __launch_bounds__(64 * kDW) __attribute__((amdgpu_waves_per_eu(4))) gemm_decode_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m, int64_t k,
     const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, int64_t n,
     const float* __restrict__ gsf_a, const float* __restrict__ gsf_b, int64_t a_seg_rows,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int splits, float* __restrict__ partial,
     const uint16_t* __restrict__ a16) {
   constexpr int kLoads = kA16 ? 5 : 6;   // direct-load instructions per super tile and wave
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][kDecDepth][kDecSlot];
-  __shared__ float red[kWaves - 1][4][64];
+  static_assert(kDW == 4 || kDW == 8, "waves per block");
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kDW][kDecDepth][kDecSlot];
 
   const int tile = blockIdx.x / splits;
   const int split = blockIdx.x % splits;
@@ -334,7 +341,7 @@ __global__ void __launch_bounds__(256) gemm_decode_kernel(
   const int64_t kt_all = (k + BK - 1) / BK;
   const int64_t st_all = (kt_all + 1) / 2;
   const int64_t b0 = st_all * split / splits, b1 = st_all * (split + 1) / splits;
-  const int64_t s0 = b0 + (b1 - b0) * wave / kWaves, s1 = b0 + (b1 - b0) * (wave + 1) / kWaves;
+  const int64_t s0 = b0 + (b1 - b0) * wave / kDW, s1 = b0 + (b1 - b0) * (wave + 1) / kDW;
   const int count = (int)(s1 - s0);
 
   // Direct-load sources.  Lines: lane l -> row lr (+ 8 for the second instruction) at
@@ -356,13 +363,16 @@ __global__ void __launch_bounds__(256) gemm_decode_kernel(
   const uint16_t* xl0 = kA16 ? a16 + min((int64_t)ar0, m - 1) * k + 8 * ac0 : nullptr;
   const uint16_t* xl1 = kA16 ? a16 + min((int64_t)ar1, m - 1) * k + 8 * ac1 : nullptr;
 
-  // Loads super tile st into a slot.  Super tiles past the wave's range re-load the last
-  // one (the slot is never multiplied); chunks past the end of a row (partial last super
-  // tile) re-load the row's first chunk, whose block scales there are the zero padding
-  // of the scale layout; the K tile past an odd count of K tiles re-loads the last one's
-  // scale words, and the lanes that own it use zero scales instead (multiply).
+  // Loads super tile st into a slot.  Super tiles past the wave's range re-load the
+  // wave's own last one (the slot is never multiplied; those lines are still in L2,
+  // while the next wave's first ones would come from HBM a second time); chunks past the
+  // end of a row (partial last super tile) re-load the row's first chunk, whose block
+  // scales there are the zero padding of the scale layout; the K tile past an odd count
+  // of K tiles re-loads the last one's scale words, and the lanes that own it use zero
+  // scales instead (multiply).
+  const int64_t st_last = min(max(s1 - 1, s0), st_all - 1);
   auto issue = [&](int64_t st, uint8_t* slot) {
-    st = min(st, st_all - 1);
+    st = min(st, st_last);
     const int64_t off = st * 128;
     const int64_t o0 = off + 16 * lc0 < half_k ? off : -16 * lc0;
     const int64_t o1 = off + 16 * lc1 < half_k ? off : -16 * lc1;
@@ -406,41 +416,44 @@ __global__ void __launch_bounds__(256) gemm_decode_kernel(
     }
   };
 
-  // Super tiles s0 + i and s0 + i + 1 from slots sa and sb.  Each slot is refilled as
-  // soon as it has been multiplied, so one super tile's loads are in flight while the
-  // other is multiplied.  The loop body has no branch; an odd last super tile is
-  // multiplied after the loop.
-  auto pair = [&](uint8_t* sa, uint8_t* sb, int i) __attribute__((always_inline)) {
-    dec_wait_one_behind<kLoads>();          // super tile s0 + i has landed
-    multiply(sa, s0 + i);
-    dec_lds_order();                // its reads are done before the slot is refilled
-    issue(s0 + i + 2, sa);
-    dec_wait_one_behind<kLoads>();
-    multiply(sb, s0 + i + 1);
-    dec_lds_order();
-    issue(s0 + i + 3, sb);
-  };
+  // Super tiles s0 + i and s0 + i + 1 from slots 0 and 1.  Each slot is refilled as soon
+  // as it has been multiplied, so one super tile's loads are in flight while the other
+  // is multiplied.  The loop body has no branch; an odd last super tile is multiplied
+  // after the loop.
   issue(s0, ring[wave][0]);
   issue(s0 + 1, ring[wave][1]);
   int i = 0;
-  for (; i + 1 < count; i += 2) pair(ring[wave][0], ring[wave][1], i);
+  for (; i + 1 < count; i += 2) {
+    dec_wait<kLoads>();                  // super tile s0 + i has landed
+    multiply(ring[wave][0], s0 + i);
+    dec_lds_order();                     // its reads are done before the slot is refilled
+    issue(s0 + i + 2, ring[wave][0]);
+    dec_wait<kLoads>();
+    multiply(ring[wave][1], s0 + i + 1);
+    dec_lds_order();
+    issue(s0 + i + 3, ring[wave][1]);
+  }
   if (i < count) {
-    dec_wait_one_behind<kLoads>();
+    dec_wait<kLoads>();
     multiply(ring[wave][0], s0 + i);
   }
   dec_wait_all();                   // nothing still landing in this wave's slots
 
-  // Sum the four waves' K quarters in wave order: ((w0 + w1) + w2) + w3.
+  // Sum the waves' K ranges in wave order: ((w0 + w1) + w2) + ...  Each wave hands its
+  // sums over in its own first slot, which no load writes any more.
+  float* red = reinterpret_cast<float*>(ring[wave][0]);
   if (wave > 0) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) red[wave - 1][e][lane] = acc[e];
+    for (int e = 0; e < 4; ++e) red[e * 64 + lane] = acc[e];
   }
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
-  for (int w = 0; w < kWaves - 1; ++w)
+  for (int w = 1; w < kDW; ++w) {
+    const float* rw = reinterpret_cast<const float*>(ring[w][0]);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] += red[w][e][lane];
+    for (int e = 0; e < 4; ++e) acc[e] += rw[e * 64 + lane];
+  }
 
   // 16x16 MFMA output: lane holds column l16, rows 4g .. 4g+3.
   const int64_t col = n0 + l16;
@@ -461,15 +474,47 @@ __global__ void __launch_bounds__(256) gemm_decode_kernel(
   }
 }
 
-// K splits of gemm_decode_kernel: enough blocks for two per compute unit, each wave
-// keeping at least two super tiles.
-int decode_splits(int64_t k, int64_t n, int cus) {
+// Launch shape of gemm_decode_kernel.  Aim: enough four-wave blocks for two per compute
+// unit, each wave keeping at least two super tiles.  Where that takes a K split and the
+// rows are short (K <= 16384: at most 8 super tiles per wave of an eight-wave block),
+// eight-wave blocks halve the split, which saves the reduce launch at a two-way split
+// (measured, one row: o_proj 11.0 -> 10.0 us, k_proj 5.8 -> 4.9 us).  On longer rows the
+// fewer, longer blocks leave the compute units unevenly loaded (down_proj, K = 25600:
+// 22.0 -> 23.1 us), so those keep four waves.
+struct DecodePlan {
+  int waves;
+  int splits;
+};
+DecodePlan decode_plan(int64_t k, int64_t n, int cus) {
   const int64_t tiles = (n + kDecRows - 1) / kDecRows;
   const int64_t st = ((k + BK - 1) / BK + 1) / 2;
   int64_t sp = (2 * cus + tiles - 1) / tiles;
-  const int64_t max_sp = st / (2 * kWaves) > 0 ? st / (2 * kWaves) : 1;
+  const int64_t max_sp = st / (2 * 4) > 0 ? st / (2 * 4) : 1;
   if (sp > max_sp) sp = max_sp;
-  return (int)(sp < 1 ? 1 : sp);
+  if (sp < 2) return {4, 1};
+  if (st > 64) return {4, (int)sp};
+  return {8, (int)(sp / 2)};
+}
+
+template <bool kA16, int kDW>
+void launch_decode_t(dim3 grid, hipStream_t s, const uint8_t* a_codes, const uint8_t* a_scales, int64_t m,
+                     int64_t k, const uint8_t* b_codes, const uint8_t* b_scales, int64_t n, const float* gsf_a,
+                     const float* gsf_b, int64_t a_seg_rows, const uint16_t* bias, uint16_t* out, int splits,
+                     float* partial, const uint16_t* x16) {
+  hipLaunchKernelGGL((gemm_decode_kernel<kA16, kDW>), grid, dim3(64 * kDW), 0, s, a_codes, a_scales, m, k, b_codes,
+                     b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, splits, partial, x16);
+}
+
+hipError_t launch_decode(bool a16, int waves, uint32_t blocks, hipStream_t s, const uint8_t* a_codes,
+                         const uint8_t* a_scales, int64_t m, int64_t k, const uint8_t* b_codes,
+                         const uint8_t* b_scales, int64_t n, const float* gsf_a, const float* gsf_b,
+                         int64_t a_seg_rows, const uint16_t* bias, uint16_t* out, int splits, float* partial,
+                         const uint16_t* x16) {
+  auto fn = a16 ? (waves == 8 ? launch_decode_t<true, 8> : launch_decode_t<true, 4>)
+                : (waves == 8 ? launch_decode_t<false, 8> : launch_decode_t<false, 4>);
+  fn(dim3(blocks), s, a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, splits,
+     partial, x16);
+  return hipGetLastError();
 }
 
 template <int MT, bool kFusedA = false>
@@ -527,7 +572,7 @@ bool gemm_skinny_supported(int64_t m, int64_t k, const void* a_codes, const void
 size_t gemm_skinny_workspace_bytes(int64_t m, int64_t k, int64_t n, int cus) {
   // m <= 16 also covers the static-scale fused launch, which splits like gemm_skinny_kernel
   int64_t sp = skinny_splits(k, n, cus);
-  if (m <= 16) sp = std::max<int64_t>(sp, decode_splits(k, n, cus));
+  if (m <= 16) sp = std::max<int64_t>(sp, decode_plan(k, n, cus).splits);
   return sp > 1 ? (size_t)sp * (size_t)m * (size_t)n * sizeof(float) : 0;
 }
 
@@ -535,17 +580,16 @@ hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales, i
                               const uint8_t* b_codes, const uint8_t* b_scales, int64_t n, const float* gsf_a,
                               const float* gsf_b, int64_t a_seg_rows, const uint16_t* bias, uint16_t* out,
                               void* workspace, size_t workspace_bytes, int cus, hipStream_t s) {
-  int splits = m <= 16 ? decode_splits(k, n, cus) : skinny_splits(k, n, cus);
+  const DecodePlan plan = decode_plan(k, n, cus);
+  int splits = m <= 16 ? plan.splits : skinny_splits(k, n, cus);
   const size_t need = splits > 1 ? (size_t)splits * (size_t)m * (size_t)n * sizeof(float) : 0;
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) splits = 1;
   float* partial = splits > 1 ? static_cast<float*>(workspace) : nullptr;
   hipError_t e;
   if (m <= 16) {
     const int64_t tiles = (n + kDecRows - 1) / kDecRows;
-    hipLaunchKernelGGL(gemm_decode_kernel<false>, dim3((uint32_t)(tiles * splits)), dim3(256), 0, s, a_codes,
-                       a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, splits, partial,
-                       (const uint16_t*)nullptr);
-    e = hipGetLastError();
+    e = launch_decode(false, plan.waves, (uint32_t)(tiles * splits), s, a_codes, a_scales, m, k, b_codes, b_scales,
+                      n, gsf_a, gsf_b, a_seg_rows, bias, out, splits, partial, nullptr);
   } else if (m <= 32) {
     e = launch_mt<2>(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, a_seg_rows, out, splits, partial, s);
   } else if (m <= 64) {
@@ -569,15 +613,14 @@ hipError_t launch_gemm_decode_a16(const uint16_t* a16, int64_t m, int64_t k, con
                                   const uint8_t* b_scales, int64_t n, const float* gsf_a, const float* gsf_b,
                                   const uint16_t* bias, uint16_t* out, void* workspace, size_t workspace_bytes,
                                   int cus, hipStream_t s) {
-  int splits = decode_splits(k, n, cus);
+  const DecodePlan plan = decode_plan(k, n, cus);
+  int splits = plan.splits;
   const size_t need = splits > 1 ? (size_t)splits * (size_t)m * (size_t)n * sizeof(float) : 0;
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) splits = 1;
   float* partial = splits > 1 ? static_cast<float*>(workspace) : nullptr;
   const int64_t tiles = (n + kDecRows - 1) / kDecRows;
-  hipLaunchKernelGGL(gemm_decode_kernel<true>, dim3((uint32_t)(tiles * splits)), dim3(256), 0, s,
-                     (const uint8_t*)nullptr, (const uint8_t*)nullptr, m, k, b_codes, b_scales, n, gsf_a, gsf_b,
-                     (int64_t)0, bias, out, splits, partial, a16);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_decode(true, plan.waves, (uint32_t)(tiles * splits), s, nullptr, nullptr, m, k, b_codes,
+                               b_scales, n, gsf_a, gsf_b, 0, bias, out, splits, partial, a16);
   if (e != hipSuccess || splits == 1) return e;
   const int64_t total = m * n;
   hipLaunchKernelGGL(gemm_skinny_reduce, dim3((uint32_t)((total + 255) / 256)), dim3(256), 0, s, partial, splits, m,

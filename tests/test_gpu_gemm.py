@@ -210,6 +210,29 @@ def test_few_rows_weight_streaming(m, n, k):
     assert_gemm_close(whole.float().cpu().numpy(), ref, bound)
 
 
+@pytest.mark.parametrize("n,k,split_k", [(1024, 5120, True), (5120, 8192, True), (4096, 5120, True),
+                                         (300, 4128, True), (301, 1056, True), (64, 96, True), (200, 25600, True),
+                                         (64, 16384, False)])
+def test_one_row_decode_equals_row_of_two(n, k, split_k):
+    """Decode rows are independent: one activation row gives the first row of the same
+    product with a second row added, bit for bit, and is within the oracle's bound.
+    Shapes: 8-wave blocks (k, o), 4-wave blocks, a partial last super tile, a single K
+    tile, a 12-way K split, and unsplit 16384-long rows on 8-wave blocks."""
+    rng = np.random.default_rng(n + 3 * k)
+    px, sx = random_operands(rng, 2, k)
+    pw, sw = random_operands(rng, n, k)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    w = (t(pw), t(canonical_to_layout(sw, k)))
+    two = nv().nvfp4_gemm(t(px), t(canonical_to_layout(sx, k)), *w, 1.5, 0.25, split_k=split_k)
+    one = nv().nvfp4_gemm(t(px[:1]), t(canonical_to_layout(sx[:1], k)), *w, 1.5, 0.25, split_k=split_k)
+    torch.cuda.synchronize()
+    assert torch.equal(one[0], two[0])
+    alpha = o.alpha_of(1.5, 0.25)
+    ref = o.nvfp4_gemm(px[:1], sx[:1], pw, sw, alpha)
+    bound = accumulation_bound(o.dequantize(px[:1], sx[:1]), o.dequantize(pw, sw), alpha)
+    assert_gemm_close(one.float().cpu().numpy(), ref, bound)
+
+
 @pytest.mark.parametrize("m,n,k", [(65, 4352, 1056), (200, 4100, 2080), (511, 1000, 640), (128, 25600, 512),
                                    (100, 65800, 256)])
 def test_mid_rows_pipelined_split(m, n, k):
