@@ -27,6 +27,10 @@ HIPCC_FLAGS = [
 ]
 
 
+# roctx profiler ranges around each call and stage (rocprofv3 --marker-trace)
+LINK_FLAGS = ["-L/opt/rocm/lib", "-lrocprofiler-sdk-roctx"]
+
+
 def hipcc() -> str:
     for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -37,7 +41,7 @@ def hipcc() -> str:
 def build(verbose: bool = False, out: str = LIB_PATH, extra_flags: list[str] | None = None) -> str:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     tmp = out + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), f"-I{INCLUDE}", "-o", tmp, *srcs]
+    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), f"-I{INCLUDE}", "-o", tmp, *srcs, *LINK_FLAGS]
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)

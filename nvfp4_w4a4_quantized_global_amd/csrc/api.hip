@@ -11,6 +11,8 @@
 
 #include <mutex>
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 #include "../../include/nvfp4.h"
 #include "nvfp4_launch.h"
 
@@ -30,6 +32,17 @@ int hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return NVFP4_OK;
   return fail(NVFP4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
+
+// Profiler ranges (roctx): one around each entry-point call, one around each stage
+// inside it (nvfp4.amax, nvfp4.quantize, nvfp4.gemm), so that a marker trace ties every
+// kernel to the call and stage that queued it.  Without a profiler a push or pop is a
+// call into an empty dispatch table.
+struct Range {
+  explicit Range(const char* name) { roctxRangePushA(name); }
+  ~Range() { roctxRangePop(); }
+  Range(const Range&) = delete;
+  Range& operator=(const Range&) = delete;
+};
 
 size_t align_up(size_t v) { return (v + NVFP4_WORKSPACE_ALIGN - 1) / NVFP4_WORKSPACE_ALIGN * NVFP4_WORKSPACE_ALIGN; }
 
@@ -134,9 +147,12 @@ int quantize_impl(const char* fn, const void* x, int64_t m, int64_t k, const flo
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   const uint16_t* upp = static_cast<const uint16_t*>(up);
   if (gsf_static == nullptr && segments == 1 && up == nullptr &&
-      nvfp4::quantize_small_supported(m, k))   // small input: both passes in one launch
+      nvfp4::quantize_small_supported(m, k)) {   // small input: both passes in one launch
+    Range stage("nvfp4.amax+quantize");
     return hip_status(nvfp4::launch_quantize_small(xp, m, k, group, c, codes, scales, gsf_out, s, a16), fn);
+  }
   if (gsf_static == nullptr) {
+    Range stage("nvfp4.amax");
     uint16_t* xout = upp != nullptr ? static_cast<uint16_t*>(xbuf) : nullptr;
     int rc = hip_status(nvfp4::launch_amax_partials(xp, upp, xout, seg_rows, k, (int)segments, group, c, partials,
                                                     &n_partials, s), fn);
@@ -146,6 +162,7 @@ int quantize_impl(const char* fn, const void* x, int64_t m, int64_t k, const flo
       upp = nullptr;
     }
   }
+  Range stage("nvfp4.quantize");
   return hip_status(nvfp4::launch_quantize(xp, upp, m, k, group, c, gsf_static, partials, n_partials, seg_rows,
                                            (int)segments, codes, scales, gsf_out, s, a16), fn);
 }
@@ -168,6 +185,7 @@ int linear_impl(const char* fn, const void* x, int64_t segments, int64_t seg_row
                 const float* global_sf_x, int rotation_group, void* out, float* gsf_out, void* workspace,
                 size_t workspace_bytes, hipStream_t s, const void* up = nullptr, bool split_k = true) {
   // a dynamic scale over a SwiGLU product keeps the product after the linear workspace
+  Range call(fn);
   const bool keep_product = up != nullptr && global_sf_x == nullptr;
   const int64_t m = segments * seg_rows;
   if (int rc = check_rows_k(fn, m, k, true)) return rc;
@@ -190,6 +208,7 @@ int linear_impl(const char* fn, const void* x, int64_t segments, int64_t seg_row
       nvfp4::linear_skinny_fused_supported(m, k, out_features, x, packed, inv_scale, nvfp4::compute_units()) &&
       ws.gemm_bytes >= nvfp4::gemm_workspace_bytes(m, k, out_features)) {
     // static scale, few rows: quantized inside the weight-streaming GEMM, one launch
+    Range stage("nvfp4.quantize+gemm");
     return hip_status(nvfp4::launch_linear_skinny_fused(static_cast<const uint16_t*>(x), m, k, packed, inv_scale,
                                                         out_features, global_sf_x, global_sf_w,
                                                         static_cast<const uint16_t*>(bias),
@@ -207,6 +226,7 @@ int linear_impl(const char* fn, const void* x, int64_t segments, int64_t seg_row
   if (int rc = quantize_impl(fn, x, m, k, global_sf_x, rotation_group, ws.codes, ws.scales, gsf, ws.partials, s,
                              per_segment ? segments : 1, up, xbuf, a16 ? ws.a16 : nullptr))
     return rc;
+  Range stage("nvfp4.gemm");
   if (a16)
     return hip_status(nvfp4::launch_gemm_decode_a16(ws.a16, m, k, packed, inv_scale, out_features, gsf, global_sf_w,
                                                     static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(out),
@@ -288,6 +308,7 @@ const char* nvfp4_last_error(void) { return g_err; }
 int rotate_activation(const void* x, int x_dtype, void* y, int y_dtype, int64_t rows, int64_t k, int group_size,
                       void* stream) {
   const char* fn = "rotate_activation";
+  Range call(fn);
   g_err[0] = 0;
   if (int rc = check_rows_k(fn, rows, k, true)) return rc;
   if (int rc = check_group(fn, group_size, k, false)) return rc;
@@ -307,6 +328,7 @@ int rotate_activation(const void* x, int x_dtype, void* y, int y_dtype, int64_t 
 int nvfp4_quantize_weight(const void* w, int64_t n, int64_t k, uint8_t* packed, uint8_t* inv_scale,
                           float* global_sf_w, void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "nvfp4_quantize_weight";
+  Range call(fn);
   g_err[0] = 0;
   if (int rc = check_rows_k(fn, n, k, false)) return rc;
   if (!w || !packed || !inv_scale || !global_sf_w) return fail(NVFP4_ERR_ARG, "%s: NULL tensor argument", fn);
@@ -325,6 +347,7 @@ int nvfp4_quantize_activation(const void* x, int64_t m, int64_t k, const float* 
                               uint8_t* codes, uint8_t* scales, float* gsf_out, void* workspace,
                               size_t workspace_bytes, void* stream) {
   const char* fn = "nvfp4_quantize_activation";
+  Range call(fn);
   g_err[0] = 0;
   if (int rc = check_rows_k(fn, m, k, true)) return rc;
   if (int rc = check_group(fn, rotation_group, k, true)) return rc;
@@ -346,6 +369,7 @@ int nvfp4_quantize_activation(const void* x, int64_t m, int64_t k, const float* 
 int nvfp4_amax(const void* x, int64_t rows, int64_t k, int rotation_group, float* amax, int accumulate,
                void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "nvfp4_amax";
+  Range call(fn);
   g_err[0] = 0;
   if (int rc = check_rows_k(fn, rows, k, true)) return rc;
   if (int rc = check_group(fn, rotation_group, k, true)) return rc;
@@ -372,6 +396,7 @@ int nvfp4_amax(const void* x, int64_t rows, int64_t k, int rotation_group, float
 
 int nvfp4_swiglu(const void* gate, const void* up, int64_t rows, int64_t k, void* x, void* stream) {
   const char* fn = "nvfp4_swiglu";
+  Range call(fn);
   g_err[0] = 0;
   if (int rc = check_rows_k(fn, rows, k, true)) return rc;
   if (rows == 0) return NVFP4_OK;
@@ -387,6 +412,7 @@ int nvfp4_quantize_swiglu(const void* gate, const void* up, int64_t m, int64_t k
                           uint8_t* codes, uint8_t* scales, float* gsf_out, void* workspace, size_t workspace_bytes,
                           void* stream) {
   const char* fn = "nvfp4_quantize_swiglu";
+  Range call(fn);
   g_err[0] = 0;
   if (int rc = check_rows_k(fn, m, k, true)) return rc;
   if (m == 0) return NVFP4_OK;
@@ -419,6 +445,7 @@ int nvfp4_linear_swiglu(const void* gate, const void* up, int64_t m, int64_t k, 
 int nvfp4_dequantize(const uint8_t* packed, const uint8_t* scales, int64_t rows, int64_t k, const float* global_sf,
                      void* out, int out_dtype, void* stream) {
   const char* fn = "nvfp4_dequantize";
+  Range call(fn);
   g_err[0] = 0;
   if (int rc = check_rows_k(fn, rows, k, true)) return rc;
   if (out_dtype != NVFP4_DTYPE_BF16 && out_dtype != NVFP4_DTYPE_F32)
@@ -435,6 +462,7 @@ int nvfp4_dequantize(const uint8_t* packed, const uint8_t* scales, int64_t rows,
 
 int nvfp4_static_global_scale(const float* amax, float margin, float* gsf, void* stream) {
   const char* fn = "nvfp4_static_global_scale";
+  Range call(fn);
   g_err[0] = 0;
   if (!amax || !gsf) return fail(NVFP4_ERR_ARG, "%s: NULL argument", fn);
   if (int rc = check_align(fn, "amax", amax, 4)) return rc;
@@ -448,6 +476,7 @@ int nvfp4_quantize_activation_segmented(const void* x, int64_t segments, int64_t
                                         int rotation_group, uint8_t* codes, uint8_t* scales, float* gsf_out,
                                         void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "nvfp4_quantize_activation_segmented";
+  Range call(fn);
   g_err[0] = 0;
   if (int rc = check_segments(fn, segments, seg_rows)) return rc;
   const int64_t m = segments * seg_rows;
@@ -470,6 +499,7 @@ int nvfp4_gemm(const uint8_t* x_codes, const uint8_t* x_scale, int64_t m, int64_
                const uint8_t* inv_scale, int64_t n, const float* gsf_x, const float* gsf_w, const void* bias,
                void* out, void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "nvfp4_gemm";
+  Range call(fn);
   g_err[0] = 0;
   if (int rc = check_rows_k(fn, m, k, true)) return rc;
   if (n <= 0 || n >= kMaxDim) return fail(NVFP4_ERR_SHAPE, "%s: out_features must be in [1, 2^31), got %lld", fn, (long long)n);
@@ -532,6 +562,7 @@ int nvfp4_linear_segmented(const void* x, int64_t segments, int64_t seg_rows, in
 
 int nvfp4_scale_to_canonical(const uint8_t* layout, uint8_t* canonical, int64_t rows, int64_t k, void* stream) {
   const char* fn = "nvfp4_scale_to_canonical";
+  Range call(fn);
   g_err[0] = 0;
   if (int rc = check_rows_k(fn, rows, k, true)) return rc;
   if (rows == 0) return NVFP4_OK;
@@ -541,6 +572,7 @@ int nvfp4_scale_to_canonical(const uint8_t* layout, uint8_t* canonical, int64_t 
 
 int nvfp4_scale_from_canonical(const uint8_t* canonical, uint8_t* layout, int64_t rows, int64_t k, void* stream) {
   const char* fn = "nvfp4_scale_from_canonical";
+  Range call(fn);
   g_err[0] = 0;
   if (int rc = check_rows_k(fn, rows, k, true)) return rc;
   if (rows == 0) return NVFP4_OK;
