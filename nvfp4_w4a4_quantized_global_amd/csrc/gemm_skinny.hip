@@ -317,18 +317,25 @@ __device__ __forceinline__ void dec_lds_order() { asm volatile("s_waitcnt lgkmcn
 // takes the place of a two-way block-level K split: the partial sums meet in LDS and the
 // second launch (gemm_skinny_reduce) is not needed.
 //
-// Four waves per SIMD (two eight-wave or four four-wave blocks per compute unit, as the
-// LDS allows) bound the registers.
-template <bool kA16, int kDW>
-__global__ void __launch_bounds__(64 * kDW) __attribute__((amdgpu_waves_per_eu(4))) gemm_decode_kernel(
+// kOne (m == 1): the slot carries the one activation row only (512 bytes: the row's 256
+// fp16 values, or its 128 code bytes and 16 scale bytes), 2816 bytes in all instead of
+// 4608, so seven four-wave blocks fit a compute unit's LDS instead of four.
+//
+// Four waves per SIMD (seven with kOne) bound the registers.
+template <bool kA16, int kDW, bool kOne>
+__global__ void __launch_bounds__(64 * kDW) __attribute__((amdgpu_waves_per_eu(kOne ? 7 : 4))) gemm_decode_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m, int64_t k,
     const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, int64_t n,
     const float* __restrict__ gsf_a, const float* __restrict__ gsf_b, int64_t a_seg_rows,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int splits, float* __restrict__ partial,
     const uint16_t* __restrict__ a16) {
-  constexpr int kLoads = kA16 ? 5 : 6;   // direct-load instructions per super tile and wave
+  // direct-load instructions per super tile and wave; bytes per slot and where the
+  // weight's scale words sit in it
+  constexpr int kLoads = kOne || kA16 ? 5 : 6;
+  constexpr int kSlot = kOne ? 2048 + 512 + 256 : kDecSlot;
+  constexpr int kOffBS = kOne ? 2560 : 4096;
   static_assert(kDW == 4 || kDW == 8, "waves per block");
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kDW][kDecDepth][kDecSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kDW][kDecDepth][kSlot];
 
   const int tile = blockIdx.x / splits;
   const int split = blockIdx.x % splits;
@@ -362,6 +369,11 @@ __global__ void __launch_bounds__(64 * kDW) __attribute__((amdgpu_waves_per_eu(4
   const int ac0 = ap ^ ar0, ac1 = ap ^ ar1;
   const uint16_t* xl0 = kA16 ? a16 + min((int64_t)ar0, m - 1) * k + 8 * ac0 : nullptr;
   const uint16_t* xl1 = kA16 ? a16 + min((int64_t)ar1, m - 1) * k + 8 * ac1 : nullptr;
+  // kOne: 4-byte pieces of row 0 in K order.  a16: lane l takes values 2 l, 2 l + 1 and
+  // 128 + 2 l, 129 + 2 l of the super tile; codes: lane l takes bytes 4 (l % 32) .. + 3 of
+  // its line (lanes 32 .. 63 repeat lanes 0 .. 31) and scale word l % 4 (K tile
+  // 2 st + (l % 4) / 2, word l % 2).
+  const int sw4 = lane & 3;
 
   // Loads super tile st into a slot.  Super tiles past the wave's range re-load the
   // wave's own last one (the slot is never multiplied; those lines are still in L2,
@@ -378,6 +390,21 @@ __global__ void __launch_bounds__(64 * kDW) __attribute__((amdgpu_waves_per_eu(4
     const int64_t o1 = off + 16 * lc1 < half_k ? off : -16 * lc1;
     dec_dma16(bl0 + o0, slot);
     dec_dma16(bl1 + o1, slot + 1024);
+    if (kOne) {
+      // pieces past the end of the row re-load its first one (zero weight scales there)
+      const int64_t kt = min(2 * st + (sw4 >> 1), kt_all - 1);
+      if (kA16) {
+        const int64_t e0 = st * 256 + 2 * lane, e1 = e0 + 128;
+        dec_dma4(reinterpret_cast<const uint8_t*>(a16 + (e0 < k ? e0 : 0)), slot + 2048);
+        dec_dma4(reinterpret_cast<const uint8_t*>(a16 + (e1 < k ? e1 : 0)), slot + 2048 + 256);
+      } else {
+        const int64_t c = off + 4 * (lane & 31);
+        dec_dma4(a_codes + (c < half_k ? c : 0), slot + 2048);
+        dec_dma4(a_scales + kt * 8 + 4 * (sw4 & 1), slot + 2048 + 256);
+      }
+      dec_dma4(bsl + min(2 * st + sh, kt_all - 1) * n * 8, slot + kOffBS);
+      return;
+    }
     if (kA16) {
       // values past the end of a row re-load the row's first chunk (zero weight scales)
       const int64_t e = st * 256;
@@ -399,11 +426,25 @@ __global__ void __launch_bounds__(64 * kDW) __attribute__((amdgpu_waves_per_eu(4
     const int p0 = (2 * g) ^ dec_swz(l16), p1 = (2 * g + 1) ^ dec_swz(l16);
     const uint4 w0 = *reinterpret_cast<const uint4*>(slot + l16 * 128 + 16 * p0);
     const uint4 w1 = *reinterpret_cast<const uint4*>(slot + l16 * 128 + 16 * p1);
-    const uint4 x0 = *reinterpret_cast<const uint4*>(slot + 2048 + l16 * 128 + 16 * p0);
-    const uint4 x1 = *reinterpret_cast<const uint4*>(slot + 2048 + l16 * 128 + 16 * p1);
     const int so = (g >> 1) * 128 + l16 * 8 + 4 * (g & 1);
     const uint32_t keep = 2 * st + (g >> 1) < kt_all ? ~0u : 0u;   // K tile exists
-    const uint32_t bs = *reinterpret_cast<const uint32_t*>(slot + 4096 + so) & keep;
+    const uint32_t bs = *reinterpret_cast<const uint32_t*>(slot + kOffBS + so) & keep;
+    if constexpr (kOne) {
+      // every lane reads row 0: K values 64 g + 8 s .. of the super tile
+      const uint4 x0 = *reinterpret_cast<const uint4*>(slot + 2048 + 32 * g);
+      const uint4 x1 = *reinterpret_cast<const uint4*>(slot + 2048 + 32 * g + 16);
+      const uint32_t as = kA16 ? 0u : *reinterpret_cast<const uint32_t*>(slot + 2048 + 256 + 4 * g) & keep;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const half8_t fb = dequant8(word(s < 4 ? w0 : w1, s & 3), scale_pair(bs, s >> 1));
+        const half8_t fa = kA16 ? *reinterpret_cast<const half8_t*>(slot + 2048 + 128 * g + 16 * s)
+                                : dequant8(word(s < 4 ? x0 : x1, s & 3), scale_pair(as, s >> 1));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fb, acc, 0, 0, 0);
+      }
+      return;
+    }
+    const uint4 x0 = *reinterpret_cast<const uint4*>(slot + 2048 + l16 * 128 + 16 * p0);
+    const uint4 x1 = *reinterpret_cast<const uint4*>(slot + 2048 + l16 * 128 + 16 * p1);
     const uint32_t as = kA16 ? 0u : *reinterpret_cast<const uint32_t*>(slot + 4096 + 256 + so) & keep;
     const int xr = l16 & 3;   // kA16: the a16 row this lane reads
 #pragma unroll
@@ -496,13 +537,13 @@ DecodePlan decode_plan(int64_t k, int64_t n, int cus) {
   return {8, (int)(sp / 2)};
 }
 
-template <bool kA16, int kDW>
+template <bool kA16, int kDW, bool kOne>
 void launch_decode_t(dim3 grid, hipStream_t s, const uint8_t* a_codes, const uint8_t* a_scales, int64_t m,
                      int64_t k, const uint8_t* b_codes, const uint8_t* b_scales, int64_t n, const float* gsf_a,
                      const float* gsf_b, int64_t a_seg_rows, const uint16_t* bias, uint16_t* out, int splits,
                      float* partial, const uint16_t* x16) {
-  hipLaunchKernelGGL((gemm_decode_kernel<kA16, kDW>), grid, dim3(64 * kDW), 0, s, a_codes, a_scales, m, k, b_codes,
-                     b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, splits, partial, x16);
+  hipLaunchKernelGGL((gemm_decode_kernel<kA16, kDW, kOne>), grid, dim3(64 * kDW), 0, s, a_codes, a_scales, m, k,
+                     b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, splits, partial, x16);
 }
 
 hipError_t launch_decode(bool a16, int waves, uint32_t blocks, hipStream_t s, const uint8_t* a_codes,
@@ -510,8 +551,14 @@ hipError_t launch_decode(bool a16, int waves, uint32_t blocks, hipStream_t s, co
                          const uint8_t* b_scales, int64_t n, const float* gsf_a, const float* gsf_b,
                          int64_t a_seg_rows, const uint16_t* bias, uint16_t* out, int splits, float* partial,
                          const uint16_t* x16) {
-  auto fn = a16 ? (waves == 8 ? launch_decode_t<true, 8> : launch_decode_t<true, 4>)
-                : (waves == 8 ? launch_decode_t<false, 8> : launch_decode_t<false, 4>);
+#ifndef NVFP4_DECODE_ONE_ROW
+#define NVFP4_DECODE_ONE_ROW 1
+#endif
+  const bool one = NVFP4_DECODE_ONE_ROW && m == 1;
+  auto fn = a16 ? (waves == 8 ? (one ? launch_decode_t<true, 8, true> : launch_decode_t<true, 8, false>)
+                              : (one ? launch_decode_t<true, 4, true> : launch_decode_t<true, 4, false>))
+                : (waves == 8 ? (one ? launch_decode_t<false, 8, true> : launch_decode_t<false, 8, false>)
+                              : (one ? launch_decode_t<false, 4, true> : launch_decode_t<false, 4, false>));
   fn(dim3(blocks), s, a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, splits,
      partial, x16);
   return hipGetLastError();
