@@ -333,10 +333,13 @@ int compute_units() {
 
 namespace {
 
-// Kernel choice by shape (operands aligned, K a multiple of 32): weight streaming while
-// the activation rows fit one pass of the weight (M <= 64, or M <= 128 with a narrow
-// weight), the pipelined 256 x 256 kernel above that.
-bool prefer_skinny(int64_t m, int64_t n) { return m <= 64 || (m <= 128 && n < 4096); }
+// Kernel choice by shape (operands aligned, K a multiple of 32): weight streaming up to
+// 32 activation rows, and up to 64 on narrow weights (N < 4096); the pipelined kernel
+// (128-row tiles up to M = 128) above that.  Measured, GEMM alone, one box: at M = 48
+// and 64 the pipelined kernel takes q_proj [8192, 5120] from 31.9-33.6 to 27.5 us and
+// gate [25600, 5120] from 65-70 to 54-55 us, while k_proj [1024, 5120] stays faster
+// streamed (14.8 vs 18.4 us); at M = 96 and 128 it takes k_proj from 24.1-25.7 to 18.4 us.
+bool prefer_skinny(int64_t m, int64_t n) { return m <= 32 || (m <= 64 && n < 4096); }
 
 }  // namespace
 
