@@ -46,8 +46,12 @@ def test_sizes():
     # ... and at K = 25600 the 256-row tiles split four ways
     assert L.nvfp4_gemm_workspace_bytes(4096, 25600, 1024) == 4 * 64 * 65536 * 4
     assert L.nvfp4_gemm_workspace_bytes(4096, 5120, 16384) == 0      # whole rounds only
-    # few rows: 16 column groups of 64, K split 5 ways (20 super tiles of 256, >= 4 per block)
-    assert L.nvfp4_gemm_workspace_bytes(100, 5120, 1024) == 5 * 100 * 1024 * 4
+    # few rows, streamed: 16 column groups of 64, K split 5 ways (20 super tiles of 256,
+    # >= 4 per block)
+    assert L.nvfp4_gemm_workspace_bytes(20, 5120, 1024) == 5 * 20 * 1024 * 4
+    # 100 rows on the pipelined kernel: 4 tiles of 128x256, each split into 20 blocks of
+    # 2 K tiles (fp32 partials of the whole 128x256 tile per block)
+    assert L.nvfp4_gemm_workspace_bytes(100, 5120, 1024) == 4 * 20 * 128 * 256 * 4
     # mid M: 8 tiles of 256x256, split 20 ways (40 K tiles, >= 2 per split)
     assert L.nvfp4_gemm_workspace_bytes(300, 5120, 1024) == 20 * 8 * 65536 * 4
     # never more partials than one tile per compute unit
