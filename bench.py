@@ -398,9 +398,14 @@ DECODE_COPIES = 4      # weight copies cycled: 4 x 73.7 MB exceeds the 256 MB la
 DECODE_REPS = 20
 
 
+GRAPH_SETTLE_REPLAYS = 3
+GRAPH_TIMED_REPLAYS = 3
+
+
 def graph_time_us(fns, reps: int) -> float:
-    """Mean time per call of fns (run in turn, reps times) captured in one HIP graph,
-    so the host's launch cost is out of the figure."""
+    """Time per call of fns (run in turn, reps times) captured in one HIP graph, so the
+    host's launch cost is out of the figure: the median over a few timed replays (each
+    a mean per call) after a few untimed ones."""
     import torch
     for f in fns:
         f()
@@ -414,15 +419,20 @@ def graph_time_us(fns, reps: int) -> float:
                 for f in fns:
                     f()
     torch.cuda.synchronize()
-    g.replay()
+    # untimed replays first: after host-side set-up the clock needs a few ms of load
+    for _ in range(GRAPH_SETTLE_REPLAYS):
+        g.replay()
     torch.cuda.synchronize()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record()
-    g.replay()
-    b.record()
-    b.synchronize()
-    return a.elapsed_time(b) / (reps * len(fns)) * 1e3
+    times = []
+    for _ in range(GRAPH_TIMED_REPLAYS):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b) / (reps * len(fns)) * 1e3)
+    return statistics.median(times)
 
 
 def decode_part(nv, workloads, dev, calls: int) -> None:
