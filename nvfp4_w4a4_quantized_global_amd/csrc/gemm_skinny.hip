@@ -321,9 +321,9 @@ __device__ __forceinline__ void dec_lds_order() { asm volatile("s_waitcnt lgkmcn
 // fp16 values, or its 128 code bytes and 16 scale bytes), 2816 bytes in all instead of
 // 4608, so seven four-wave blocks fit a compute unit's LDS instead of four.
 //
-// Four waves per SIMD (seven with kOne) bound the registers.
+// Four waves per SIMD (seven for four-wave blocks with kOne) bound the registers.
 template <bool kA16, int kDW, bool kOne>
-__global__ void __launch_bounds__(64 * kDW) __attribute__((amdgpu_waves_per_eu(kOne ? 7 : 4))) gemm_decode_kernel(
+__global__ void __launch_bounds__(64 * kDW) __attribute__((amdgpu_waves_per_eu(kOne && kDW == 4 ? 7 : 4))) gemm_decode_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m, int64_t k,
     const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, int64_t n,
     const float* __restrict__ gsf_a, const float* __restrict__ gsf_b, int64_t a_seg_rows,

@@ -11,6 +11,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "gemm_common.h"
 #include "nvfp4_device.h"
 #include "nvfp4_launch.h"
@@ -34,7 +36,7 @@ constexpr int kThreads = 256;
 #define NVFP4_QUANT_BLOCKS 2048
 #endif
 #ifndef NVFP4_SMALL_QUANT_VALUES
-#define NVFP4_SMALL_QUANT_VALUES 65536
+#define NVFP4_SMALL_QUANT_VALUES 131072
 #endif
 constexpr int kAmaxBlocks = NVFP4_AMAX_BLOCKS;   // partial maxima of the amax pass (<= kMaxAmaxPartials)
 static_assert(4 * kAmaxBlocks <= kMaxAmaxPartials, "partials buffer");   // SwiGLU: 4x the grid
@@ -257,12 +259,20 @@ __global__ void __launch_bounds__(kThreads) quantize_kernel(
   }
 }
 
-// Dynamic-scale quantize of a small input in one launch: one workgroup computes the
-// abs-max of the whole (rotated) input, forms the global scale and quantizes, so the
-// two passes above cost one launch instead of two.  For inputs of at most
-// kSmallQuantValues values, where launch and ramp time outweigh the streaming.
+// Dynamic-scale quantize of a small input in one launch: every workgroup computes the
+// abs-max of the whole (rotated) input by itself (the input is small and sits in L2),
+// forms the global scale and quantizes its share of the units, so the two passes above
+// cost one launch and no workgroup waits for another.  The maxima agree bit for bit (a
+// max does not depend on order), so every workgroup uses the same scale.  For inputs
+// of at most kSmallQuantValues values, where launch and ramp time outweigh the
+// streaming; one workgroup per kSmallThreads / 8 units, at most kSmallBlocks.
 constexpr int kSmallThreads = 1024;
 constexpr int64_t kSmallQuantValues = NVFP4_SMALL_QUANT_VALUES;
+#ifndef NVFP4_SMALL_QUANT_BLOCKS
+#define NVFP4_SMALL_QUANT_BLOCKS 16
+#endif
+constexpr int kSmallBlocks = NVFP4_SMALL_QUANT_BLOCKS;
+constexpr int kSmallUnroll = 4;   // pass-1 chunks in flight per lane
 
 template <bool kRotate>
 __global__ void __launch_bounds__(kSmallThreads) quantize_small_kernel(
@@ -271,22 +281,41 @@ __global__ void __launch_bounds__(kSmallThreads) quantize_small_kernel(
     uint16_t* __restrict__ a16) {
   __shared__ float lds[kSmallThreads / 64];
   const int t = threadIdx.x;
-  // pass 1: consecutive lanes take consecutive 16-value chunks (a rotation group's
-  // chunks sit in consecutive, aligned lanes)
+  // pass 1, the whole input in every workgroup: consecutive lanes take consecutive
+  // 16-value chunks (a rotation group's chunks sit in consecutive, aligned lanes).  Past
+  // one chunk per lane, kSmallUnroll chunks per lane are loaded before any is reduced.
   const int64_t n_chunks = m_rows * k / kBlock;
   float mx = 0.0f;
-  for (int64_t c0 = 0; c0 < n_chunks; c0 += kSmallThreads) {
-    const int64_t c = c0 + t;
+  auto chunk_max = [&](float (&v)[16]) {
+    if (kRotate) rotate16_bf16(v, group, inv_sqrt_g);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(v[i]));
+  };
+  if (n_chunks <= kSmallThreads) {
     float v[16];
-    if (c < n_chunks) {
-      load16_bf16(x + c * kBlock, v);
+    if (t < n_chunks) {
+      load16_bf16(x + (int64_t)t * kBlock, v);
     } else {
 #pragma unroll
       for (int i = 0; i < 16; ++i) v[i] = 0.0f;
     }
-    if (kRotate) rotate16_bf16(v, group, inv_sqrt_g);
+    chunk_max(v);
+  } else {
+    for (int64_t c0 = 0; c0 < n_chunks; c0 += kSmallUnroll * kSmallThreads) {
+      float v[kSmallUnroll][16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(v[i]));
+      for (int u = 0; u < kSmallUnroll; ++u) {
+        const int64_t c = c0 + u * kSmallThreads + t;
+        if (c < n_chunks) {
+          load16_bf16(x + c * kBlock, v[u]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) v[u][i] = 0.0f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kSmallUnroll; ++u) chunk_max(v[u]);
+    }
   }
   mx = wave_max(mx);
   if ((t & 63) == 0) lds[t >> 6] = mx;
@@ -295,12 +324,14 @@ __global__ void __launch_bounds__(kSmallThreads) quantize_small_kernel(
 #pragma unroll
   for (int i = 0; i < kSmallThreads / 64; ++i) amax = fmaxf(amax, lds[i]);
   const float gsf = global_scale_from_amax(amax);
-  if (t == 0 && gsf_out != nullptr) *gsf_out = gsf;
-  // pass 2: the units of quantize_kernel, eight lanes each (the input is re-read from L2)
+  if (t == 0 && blockIdx.x == 0 && gsf_out != nullptr) *gsf_out = gsf;
+  // pass 2: this workgroup's units of quantize_kernel, eight lanes each (the input is
+  // re-read from L2)
   const int64_t kt_count = (k + kScaleTileK - 1) / kScaleTileK;
   const int64_t units = m_rows * kt_count;
   const int j = t & 7;
-  for (int64_t u0 = 0; u0 < units; u0 += kSmallThreads / 8) {
+  for (int64_t u0 = (int64_t)blockIdx.x * (kSmallThreads / 8); u0 < units;
+       u0 += (int64_t)gridDim.x * (kSmallThreads / 8)) {
     const int64_t unit = u0 + (t >> 3);
     const int64_t row = unit / kt_count, kt = unit - row * kt_count;
     const int64_t blk = kt * 8 + j;
@@ -485,12 +516,15 @@ bool quantize_small_supported(int64_t rows, int64_t k) { return rows * k <= kSma
 
 hipError_t launch_quantize_small(const uint16_t* x, int64_t rows, int64_t k, int group, float inv_sqrt_g,
                                  uint8_t* codes, uint8_t* scales, float* gsf_out, hipStream_t s, uint16_t* a16) {
+  const int64_t units = rows * ((k + kScaleTileK - 1) / kScaleTileK);
+  const int64_t want = (units + kSmallThreads / 8 - 1) / (kSmallThreads / 8);
+  const dim3 grid((uint32_t)std::max<int64_t>(1, std::min<int64_t>(want, kSmallBlocks)));
   if (group > 1)
-    hipLaunchKernelGGL(quantize_small_kernel<true>, dim3(1), dim3(kSmallThreads), 0, s, x, rows, k, group, inv_sqrt_g,
+    hipLaunchKernelGGL(quantize_small_kernel<true>, grid, dim3(kSmallThreads), 0, s, x, rows, k, group, inv_sqrt_g,
                        codes, scales, gsf_out, a16);
   else
-    hipLaunchKernelGGL(quantize_small_kernel<false>, dim3(1), dim3(kSmallThreads), 0, s, x, rows, k, group,
-                       inv_sqrt_g, codes, scales, gsf_out, a16);
+    hipLaunchKernelGGL(quantize_small_kernel<false>, grid, dim3(kSmallThreads), 0, s, x, rows, k, group, inv_sqrt_g,
+                       codes, scales, gsf_out, a16);
   return hipGetLastError();
 }
 

@@ -205,11 +205,14 @@ def test_dequantized_weight_of_a_layer():
     assert np.array_equal(got, o.dequantize_values(pw, sw, gw))
 
 
-@pytest.mark.parametrize("m,k,g", [(16, 4096, 0), (17, 4096, 0), (1, 65536, 16), (2, 32768, 128), (4, 16400, 0),
-                                   (4096, 16, 0), (1, 5120, 0), (3, 25600, 16)])
+@pytest.mark.parametrize("m,k,g", [(32, 4096, 0), (33, 4096, 0), (1, 131072, 16), (2, 65536, 128), (8, 16400, 0),
+                                   (8192, 16, 0), (1, 5120, 0), (3, 25600, 16), (16, 5120, 0), (24, 5120, 16),
+                                   (12, 5120, 0), (25, 5120, 0), (5, 48, 2), (2048, 64, 32)])
 def test_single_launch_small_dynamic_quantize(m, k, g):
-    """Dynamic scale on inputs of at most 2^16 values takes the single-launch quantizer
-    (abs-max, scale and codes in one workgroup); larger ones the two passes.  Both sides
-    of the threshold are bit-exact against the oracle, with and without rotation."""
+    """Dynamic scale on inputs of at most 2^17 values takes the single-launch quantizer
+    (every workgroup takes the abs-max of the whole input itself, then quantizes its
+    share; up to 16 workgroups); larger ones the two passes.  Both sides of the
+    threshold, one and several workgroups, are bit-exact against the oracle, with and
+    without rotation."""
     x = workloads.draw("t3", (m, k), m + k + g, 5)
     assert_same(gpu_quantize(x, None, g), oracle_expected(x, None, g), f"{m}x{k} g{g}")
