@@ -287,7 +287,7 @@ __device__ __forceinline__ int dec_swz(int r) { return (r >> 1) & 7; }
 // dst is wave-uniform and goes to M0).  Written as inline asm so that the compiler does
 // not track these loads: it would otherwise make every LDS read of the ring wait for all
 // of them (it cannot tell the slots apart across loop iterations).  The kernel waits for
-// them itself (dec_wait_*).  The LDS address is an M0 input operand, so the compiler
+// them itself (dec_wait, dec_wait_all).  The LDS address is an M0 input operand, so the compiler
 // itself sets M0 and knows what it holds.
 __device__ __forceinline__ void dec_dma16(const uint8_t* src, uint8_t* dst) {
   asm volatile("global_load_lds_dwordx4 %1, off" :: "{m0}"((uint32_t)(uintptr_t)dst), "v"(src) : "memory");
@@ -323,7 +323,8 @@ __device__ __forceinline__ void dec_lds_order() { asm volatile("s_waitcnt lgkmcn
 //
 // Four waves per SIMD (seven for four-wave blocks with kOne) bound the registers.
 template <bool kA16, int kDW, bool kOne>
-__global__ void __launch_bounds__(64 * kDW) __attribute__((amdgpu_waves_per_eu(kOne && kDW == 4 ? 7 : 4))) gemm_decode_kernel(
+__global__ void __launch_bounds__(64 * kDW) __attribute__((amdgpu_waves_per_eu(kOne && kDW == 4 ? 7 : 4)))
+gemm_decode_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m, int64_t k,
     const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, int64_t n,
     const float* __restrict__ gsf_a, const float* __restrict__ gsf_b, int64_t a_seg_rows,
