@@ -204,12 +204,16 @@ int linear_impl(const char* fn, const void* x, int64_t segments, int64_t seg_row
     return fail(NVFP4_ERR_WORKSPACE, "%s: need a %d-byte aligned workspace of %zu bytes, got %zu", fn,
                 NVFP4_WORKSPACE_ALIGN, need, workspace_bytes);
   const LinearWorkspace ws = carve(workspace, m, k, out_features, segments, split_k);
-  if (global_sf_x != nullptr && rotation_group == 0 && up == nullptr && segments == 1 && gsf_out == nullptr &&
-      nvfp4::linear_skinny_fused_supported(m, k, out_features, x, packed, inv_scale, nvfp4::compute_units()) &&
-      ws.gemm_bytes >= nvfp4::gemm_workspace_bytes(m, k, out_features)) {
-    // static scale, few rows: quantized inside the weight-streaming GEMM, one launch
+#ifndef NVFP4_FUSED_STATIC_DECODE
+#define NVFP4_FUSED_STATIC_DECODE 1
+#endif
+  if (NVFP4_FUSED_STATIC_DECODE && global_sf_x != nullptr && rotation_group == 0 && up == nullptr &&
+      segments == 1 && gsf_out == nullptr &&
+      nvfp4::linear_decode_fused_supported(m, k, out_features, x, packed, inv_scale, ws.gemm_bytes,
+                                           nvfp4::compute_units())) {
+    // static scale, one row: quantized by the decode GEMM's waves themselves, one launch
     Range stage("nvfp4.quantize+gemm");
-    return hip_status(nvfp4::launch_linear_skinny_fused(static_cast<const uint16_t*>(x), m, k, packed, inv_scale,
+    return hip_status(nvfp4::launch_linear_decode_fused(static_cast<const uint16_t*>(x), k, packed, inv_scale,
                                                         out_features, global_sf_x, global_sf_w,
                                                         static_cast<const uint16_t*>(bias),
                                                         static_cast<uint16_t*>(out), ws.gemm, ws.gemm_bytes,

@@ -40,14 +40,8 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 constexpr int kCols = 64;            // output columns per block (4 MFMA tiles of 16)
 constexpr int kWaves = 4;
 
-// kFusedA (MT == 1): A arrives as bf16 values (a_bf16, [m][k], m <= 16) with a static
-// global scale (*gsf_a).  The block first quantizes its K range of A into LDS, each
-// 16-block once and exactly as the quantize kernel would, and the waves then read A's
-// codes and scales from LDS instead of global memory.
-constexpr int kFusedMaxSt = 16;   // super tiles of A one block can stage
-template <int MT, bool kFusedA>   // M tiles of 16 rows
+template <int MT>   // M tiles of 16 rows
 __global__ void __launch_bounds__(256) gemm_skinny_kernel(
-    const uint16_t* __restrict__ a_bf16,
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m, int64_t k,
     const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, int64_t n,
     const float* __restrict__ gsf_a, const float* __restrict__ gsf_b, int64_t a_seg_rows,
@@ -81,10 +75,8 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
     const int64_t r = min((int64_t)(16 * i + l16), m - 1);
-    if (!kFusedA) {
-      arow[i] = a_codes + r * half_k;
-      asrow[i] = a_scales + r * 8 + 4 * (g & 1);
-    }
+    arow[i] = a_codes + r * half_k;
+    asrow[i] = a_scales + r * 8 + 4 * (g & 1);
   }
 
   float4_t acc[MT][4];
@@ -119,20 +111,11 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(
     const int64_t off = st * 128 + 32 * g;
     const int64_t kt = 2 * st + (g >> 1);
     const bool c0 = off < half_k, c1 = off + 16 < half_k, sv = kt < kt_all;
-    (void)c0; (void)c1; (void)sv;
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
-      if (kFusedA) {
-        // staged rows: code bytes [128 ls + 32 g, +32) and scale bytes [16 ls + 4 g, +4)
-        const int ls = (int)(st - st_begin);
-        T.ac[i][0] = *reinterpret_cast<const uint4*>(arow[i] + ls * 128 + 32 * g);
-        T.ac[i][1] = *reinterpret_cast<const uint4*>(arow[i] + ls * 128 + 32 * g + 16);
-        T.as[i] = *reinterpret_cast<const uint32_t*>(asrow[i] + ls * 16 + 4 * g);
-      } else {
-        T.ac[i][0] = c0 ? *reinterpret_cast<const uint4*>(arow[i] + off) : make_uint4(0, 0, 0, 0);
-        T.ac[i][1] = c1 ? *reinterpret_cast<const uint4*>(arow[i] + off + 16) : make_uint4(0, 0, 0, 0);
-        T.as[i] = sv ? *reinterpret_cast<const uint32_t*>(asrow[i] + kt * m * 8) : 0u;
-      }
+      T.ac[i][0] = c0 ? *reinterpret_cast<const uint4*>(arow[i] + off) : make_uint4(0, 0, 0, 0);
+      T.ac[i][1] = c1 ? *reinterpret_cast<const uint4*>(arow[i] + off + 16) : make_uint4(0, 0, 0, 0);
+      T.as[i] = sv ? *reinterpret_cast<const uint32_t*>(asrow[i] + kt * m * 8) : 0u;
     }
   };
   auto multiply = [&](const Tile& T) {
@@ -155,32 +138,8 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(
   };
   int64_t st = st_begin + wave;
   Tile cur;
-  if (st < st_end) fetch_b(st, cur);   // the first weight loads are in flight while A is staged
-  if constexpr (kFusedA) {  // quantize this block's K range of A into LDS
-    __shared__ __attribute__((aligned(16))) uint8_t a_codes_lds[16][kFusedMaxSt * 128];
-    __shared__ __attribute__((aligned(16))) uint8_t a_scales_lds[16][kFusedMaxSt * 16];
-    const float gsf_q = *gsf_a;
-    const int nblk = (int)(st_end - st_begin) * 16;        // 16-blocks of this K range per row
-    for (int q = threadIdx.x; q < m * nblk; q += 256) {
-      const int r = q / nblk, b = q - r * nblk;
-      const int64_t e0 = (st_begin * 16 + b) * (int64_t)kBlock;
-      float v[16];
-      if (e0 < k) {
-        load16_bf16(a_bf16 + r * k + e0, v);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = 0.0f;
-      }
-      uint32_t w0, w1;
-      a_scales_lds[r][b] = (uint8_t)quantize_block16(v, gsf_q, e0 < k, w0, w1);
-      *reinterpret_cast<uint2*>(&a_codes_lds[r][b * 8]) = make_uint2(w0, w1);
-    }
-    __syncthreads();
-    arow[0] = &a_codes_lds[min((int64_t)l16, m - 1)][0];
-    asrow[0] = &a_scales_lds[min((int64_t)l16, m - 1)][0];
-  }
   if (st < st_end) {
-    fetch_a(st, cur);
+    fetch(st, cur);
     for (; st < st_end; st += kWaves) {
       Tile nxt;
       if (st + kWaves < st_end) fetch(st + kWaves, nxt);
@@ -299,9 +258,10 @@ __device__ __forceinline__ void dec_dma4(const uint8_t* src, uint8_t* dst) {
 // flight; the compiler moves no memory access across it.
 template <int kCount>
 __device__ __forceinline__ void dec_wait() {
-  static_assert(kDecDepth == 2 && (kCount == 5 || kCount == 6), "wait count");
+  static_assert(kDecDepth == 2 && (kCount == 3 || kCount == 5 || kCount == 6), "wait count");
   if constexpr (kCount == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+  else if constexpr (kCount == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
 }
 __device__ __forceinline__ void dec_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void dec_lds_order() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
@@ -321,10 +281,21 @@ __device__ __forceinline__ void dec_lds_order() { asm volatile("s_waitcnt lgkmcn
 // fp16 values, or its 128 code bytes and 16 scale bytes), 2816 bytes in all instead of
 // 4608, so seven four-wave blocks fit a compute unit's LDS instead of four.
 //
-// Four waves per SIMD (seven for four-wave blocks with kOne) bound the registers.
-template <bool kA16, int kDW, bool kOne>
-__global__ void __launch_bounds__(64 * kDW) __attribute__((amdgpu_waves_per_eu(kOne && kDW == 4 ? 7 : 4)))
-gemm_decode_kernel(
+// kFuse (with kA16 and kOne: the static-scale linear at one row): a16 points at the bf16
+// row x itself and gsf_a at its static global scale.  Each wave first quantizes its K
+// range of x (fuse_max_st super tiles at most) with the quantize kernels' block encoder
+// and keeps the fp16 operand form in its own LDS region, bit for bit what the quantize
+// pass would have written; the slots then carry only the weight (2304 bytes).  The
+// linear is one launch instead of two.
+//
+// Four waves per SIMD (seven for four-wave blocks with kOne, five with kFuse) bound the
+// registers.
+// Super tiles of x one wave quantizes: its region is 512 bytes each.  Five four-wave
+// blocks (six super tiles) or two eight-wave blocks (eight) fit a compute unit's LDS.
+constexpr int fuse_max_st(int waves) { return waves == 8 ? 8 : 6; }
+template <bool kA16, int kDW, bool kOne, bool kFuse = false>
+__global__ void __launch_bounds__(64 * kDW)
+__attribute__((amdgpu_waves_per_eu(kFuse && kDW == 4 ? 5 : kOne && kDW == 4 ? 7 : 4))) gemm_decode_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m, int64_t k,
     const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, int64_t n,
     const float* __restrict__ gsf_a, const float* __restrict__ gsf_b, int64_t a_seg_rows,
@@ -332,11 +303,13 @@ gemm_decode_kernel(
     const uint16_t* __restrict__ a16) {
   // direct-load instructions per super tile and wave; bytes per slot and where the
   // weight's scale words sit in it
-  constexpr int kLoads = kOne || kA16 ? 5 : 6;
-  constexpr int kSlot = kOne ? 2048 + 512 + 256 : kDecSlot;
-  constexpr int kOffBS = kOne ? 2560 : 4096;
+  constexpr int kLoads = kFuse ? 3 : kOne || kA16 ? 5 : 6;
+  constexpr int kSlot = kFuse ? 2048 + 256 : kOne ? 2048 + 512 + 256 : kDecSlot;
+  constexpr int kOffBS = kFuse ? 2048 : kOne ? 2560 : 4096;
   static_assert(kDW == 4 || kDW == 8, "waves per block");
+  static_assert(!kFuse || (kA16 && kOne), "the fused static-scale row is a one-row fp16 operand");
   __shared__ __attribute__((aligned(16))) uint8_t ring[kDW][kDecDepth][kSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t arow[kFuse ? kDW : 1][kFuse ? fuse_max_st(kDW) * 512 : 16];
 
   const int tile = blockIdx.x / splits;
   const int split = blockIdx.x % splits;
@@ -391,6 +364,10 @@ gemm_decode_kernel(
     const int64_t o1 = off + 16 * lc1 < half_k ? off : -16 * lc1;
     dec_dma16(bl0 + o0, slot);
     dec_dma16(bl1 + o1, slot + 1024);
+    if (kFuse) {
+      dec_dma4(bsl + min(2 * st + sh, kt_all - 1) * n * 8, slot + kOffBS);
+      return;
+    }
     if (kOne) {
       // pieces past the end of the row re-load its first one (zero weight scales there)
       const int64_t kt = min(2 * st + (sw4 >> 1), kt_all - 1);
@@ -430,6 +407,17 @@ gemm_decode_kernel(
     const int so = (g >> 1) * 128 + l16 * 8 + 4 * (g & 1);
     const uint32_t keep = 2 * st + (g >> 1) < kt_all ? ~0u : 0u;   // K tile exists
     const uint32_t bs = *reinterpret_cast<const uint32_t*>(slot + kOffBS + so) & keep;
+    if constexpr (kFuse) {
+      // every lane reads row 0 from the wave's quantized region
+      const uint8_t* xa = arow[wave] + (st - s0) * 512 + 128 * g;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const half8_t fb = dequant8(word(s < 4 ? w0 : w1, s & 3), scale_pair(bs, s >> 1));
+        const half8_t fa = *reinterpret_cast<const half8_t*>(xa + 16 * s);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fb, acc, 0, 0, 0);
+      }
+      return;
+    }
     if constexpr (kOne) {
       // every lane reads row 0: K values 64 g + 8 s .. of the super tile
       const uint4 x0 = *reinterpret_cast<const uint4*>(slot + 2048 + 32 * g);
@@ -462,8 +450,48 @@ gemm_decode_kernel(
   // as it has been multiplied, so one super tile's loads are in flight while the other
   // is multiplied.  The loop body has no branch; an odd last super tile is multiplied
   // after the loop.
+  if constexpr (kFuse) {
+    // the wave's K range of x as bf16 straight into its region, ahead of the weight
+    // loads, two super tiles (1 KB) per load; pieces past the end of the row re-load its
+    // start and are not used
+    const uint8_t* xb = reinterpret_cast<const uint8_t*>(a16);
+    for (int j = 0; j < (count + 1) / 2; ++j) {
+      const int64_t e = s0 * 256 + j * 512 + 8 * lane;
+      dec_dma16(xb + 2 * (e < k ? e : 0), arow[wave] + j * 1024);
+    }
+  }
   issue(s0, ring[wave][0]);
   issue(s0 + 1, ring[wave][1]);
+  if constexpr (kFuse) {
+    // x has landed once only the two super tiles' weight loads can be in flight; each
+    // lane then turns 16-value blocks of it into their fp16 operand form in place (a
+    // block's 32 bf16 bytes become its 32 fp16 bytes); blocks past the end of the row
+    // are zero
+    dec_wait<2 * kLoads>();
+    const float gsf_x = *gsf_a;
+    const int blocks = count * 16;
+#pragma unroll
+    for (int h = 0; h < (fuse_max_st(kDW) * 16 + 63) / 64; ++h) {
+      const int b = h * 64 + lane;
+      if (b < blocks) {
+        uint8_t* blk = arow[wave] + 32 * b;
+        const bool valid = s0 * 256 + (int64_t)b * 16 < k;
+        float v[16];
+        if (valid) {
+          load16_bf16(reinterpret_cast<const uint16_t*>(blk), v);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) v[i] = 0.0f;
+        }
+        uint32_t c0, c1;
+        const uint32_t s8 = quantize_block16(v, gsf_x, valid, c0, c1);
+        const half2_t sc = as_half2((s8 << 7) | (s8 << 23));
+        uint4* d = reinterpret_cast<uint4*>(blk);
+        d[0] = __builtin_bit_cast(uint4, dequant8(c0, sc));
+        d[1] = __builtin_bit_cast(uint4, dequant8(c1, sc));
+      }
+    }
+  }
   int i = 0;
   for (; i + 1 < count; i += 2) {
     dec_wait<kLoads>();                  // super tile s0 + i has landed
@@ -538,16 +566,16 @@ DecodePlan decode_plan(int64_t k, int64_t n, int cus) {
   return {8, (int)(sp / 2)};
 }
 
-template <bool kA16, int kDW, bool kOne>
+template <bool kA16, int kDW, bool kOne, bool kFuse = false>
 void launch_decode_t(dim3 grid, hipStream_t s, const uint8_t* a_codes, const uint8_t* a_scales, int64_t m,
                      int64_t k, const uint8_t* b_codes, const uint8_t* b_scales, int64_t n, const float* gsf_a,
                      const float* gsf_b, int64_t a_seg_rows, const uint16_t* bias, uint16_t* out, int splits,
                      float* partial, const uint16_t* x16) {
-  hipLaunchKernelGGL((gemm_decode_kernel<kA16, kDW, kOne>), grid, dim3(64 * kDW), 0, s, a_codes, a_scales, m, k,
+  hipLaunchKernelGGL((gemm_decode_kernel<kA16, kDW, kOne, kFuse>), grid, dim3(64 * kDW), 0, s, a_codes, a_scales, m, k,
                      b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, splits, partial, x16);
 }
 
-hipError_t launch_decode(bool a16, int waves, uint32_t blocks, hipStream_t s, const uint8_t* a_codes,
+hipError_t launch_decode(bool a16, bool fuse, int waves, uint32_t blocks, hipStream_t s, const uint8_t* a_codes,
                          const uint8_t* a_scales, int64_t m, int64_t k, const uint8_t* b_codes,
                          const uint8_t* b_scales, int64_t n, const float* gsf_a, const float* gsf_b,
                          int64_t a_seg_rows, const uint16_t* bias, uint16_t* out, int splits, float* partial,
@@ -556,7 +584,7 @@ hipError_t launch_decode(bool a16, int waves, uint32_t blocks, hipStream_t s, co
 #define NVFP4_DECODE_ONE_ROW 1
 #endif
   const bool one = NVFP4_DECODE_ONE_ROW && m == 1;
-  auto fn = a16 ? (waves == 8 ? (one ? launch_decode_t<true, 8, true> : launch_decode_t<true, 8, false>)
+  auto fn = fuse ? (waves == 8 ? launch_decode_t<true, 8, true, true> : launch_decode_t<true, 4, true, true>) : a16 ? (waves == 8 ? (one ? launch_decode_t<true, 8, true> : launch_decode_t<true, 8, false>)
                               : (one ? launch_decode_t<true, 4, true> : launch_decode_t<true, 4, false>))
                 : (waves == 8 ? (one ? launch_decode_t<false, 8, true> : launch_decode_t<false, 8, false>)
                               : (one ? launch_decode_t<false, 4, true> : launch_decode_t<false, 4, false>));
@@ -565,51 +593,17 @@ hipError_t launch_decode(bool a16, int waves, uint32_t blocks, hipStream_t s, co
   return hipGetLastError();
 }
 
-template <int MT, bool kFusedA = false>
+template <int MT>
 hipError_t launch_mt(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m, int64_t k, const uint8_t* b_codes,
                      const uint8_t* b_scales, int64_t n, const float* gsf_a, const float* gsf_b, const uint16_t* bias,
-                     int64_t a_seg_rows, uint16_t* out, int splits, float* partial, hipStream_t s,
-                     const uint16_t* a_bf16 = nullptr) {
+                     int64_t a_seg_rows, uint16_t* out, int splits, float* partial, hipStream_t s) {
   const int64_t groups = (n + kCols - 1) / kCols;
-  hipLaunchKernelGGL((gemm_skinny_kernel<MT, kFusedA>), dim3((uint32_t)(groups * splits)), dim3(256), 0, s, a_bf16,
-                     a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, splits,
+  hipLaunchKernelGGL((gemm_skinny_kernel<MT>), dim3((uint32_t)(groups * splits)), dim3(256), 0, s, a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, splits,
                      partial);
   return hipGetLastError();
 }
 
 }  // namespace
-
-bool linear_skinny_fused_supported(int64_t m, int64_t k, int64_t n, const void* x, const void* b_codes,
-                                   const void* b_scales, int cus) {
-  const int64_t st_all = ((k + BK - 1) / BK + 1) / 2;
-  const int sp = skinny_splits(k, n, cus);
-  const int64_t range = (st_all + sp - 1) / sp;     // super tiles a block stages
-  // staging costs about one 16-block per thread and row on the critical path: worth it
-  // while it stays within two per thread (measured: one row gains a launch, 16 rows lose),
-  // and only for small weights: on larger ones the streaming of gemm_decode_kernel gains
-  // more than the launch (measured, one row: k_proj 8.3 vs 9.0 us, q_proj 13.3 vs 11.8 us)
-  return m >= 1 && m <= 16 && k % 32 == 0 && (((uintptr_t)x | (uintptr_t)b_codes) & 15) == 0 &&
-         ((uintptr_t)b_scales & 3) == 0 && range <= kFusedMaxSt && m * range * 16 <= 2 * 256 &&
-         n * k <= ((int64_t)1 << 23);
-}
-
-hipError_t launch_linear_skinny_fused(const uint16_t* x, int64_t m, int64_t k, const uint8_t* b_codes,
-                                      const uint8_t* b_scales, int64_t n, const float* gsf_x, const float* gsf_w,
-                                      const uint16_t* bias, uint16_t* out, void* workspace, size_t workspace_bytes,
-                                      int cus, hipStream_t s) {
-  // the K range each block stages must fit its LDS: without the workspace for the
-  // planned split the caller takes the two-pass path
-  const int splits = skinny_splits(k, n, cus);
-  const size_t need = splits > 1 ? (size_t)splits * (size_t)m * (size_t)n * sizeof(float) : 0;
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return hipErrorInvalidValue;
-  float* partial = splits > 1 ? static_cast<float*>(workspace) : nullptr;
-  hipError_t e = launch_mt<1, true>(nullptr, nullptr, m, k, b_codes, b_scales, n, gsf_x, gsf_w, bias, 0, out, splits,
-                                    partial, s, x);
-  if (e != hipSuccess || splits == 1) return e;
-  hipLaunchKernelGGL(gemm_skinny_reduce, dim3((uint32_t)((m * n + 255) / 256)), dim3(256), 0, s, partial, splits, m,
-                     n, gsf_x, gsf_w, (int64_t)0, bias, out);
-  return hipGetLastError();
-}
 
 bool gemm_skinny_supported(int64_t m, int64_t k, const void* a_codes, const void* a_scales, const void* b_codes,
                            const void* b_scales) {
@@ -618,9 +612,8 @@ bool gemm_skinny_supported(int64_t m, int64_t k, const void* a_codes, const void
 }
 
 size_t gemm_skinny_workspace_bytes(int64_t m, int64_t k, int64_t n, int cus) {
-  // m <= 16 also covers the static-scale fused launch, which splits like gemm_skinny_kernel
-  int64_t sp = skinny_splits(k, n, cus);
-  if (m <= 16) sp = std::max<int64_t>(sp, decode_plan(k, n, cus).splits);
+  // up to 16 rows gemm_decode_kernel runs, split by its own plan
+  const int64_t sp = m <= 16 ? decode_plan(k, n, cus).splits : skinny_splits(k, n, cus);
   return sp > 1 ? (size_t)sp * (size_t)m * (size_t)n * sizeof(float) : 0;
 }
 
@@ -636,7 +629,7 @@ hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales, i
   hipError_t e;
   if (m <= 16) {
     const int64_t tiles = (n + kDecRows - 1) / kDecRows;
-    e = launch_decode(false, plan.waves, (uint32_t)(tiles * splits), s, a_codes, a_scales, m, k, b_codes, b_scales,
+    e = launch_decode(false, false, plan.waves, (uint32_t)(tiles * splits), s, a_codes, a_scales, m, k, b_codes, b_scales,
                       n, gsf_a, gsf_b, a_seg_rows, bias, out, splits, partial, nullptr);
   } else if (m <= 32) {
     e = launch_mt<2>(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, a_seg_rows, out, splits, partial, s);
@@ -667,12 +660,50 @@ hipError_t launch_gemm_decode_a16(const uint16_t* a16, int64_t m, int64_t k, con
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) splits = 1;
   float* partial = splits > 1 ? static_cast<float*>(workspace) : nullptr;
   const int64_t tiles = (n + kDecRows - 1) / kDecRows;
-  hipError_t e = launch_decode(true, plan.waves, (uint32_t)(tiles * splits), s, nullptr, nullptr, m, k, b_codes,
-                               b_scales, n, gsf_a, gsf_b, 0, bias, out, splits, partial, a16);
+  hipError_t e = launch_decode(true, false, plan.waves, (uint32_t)(tiles * splits), s, nullptr, nullptr, m, k,
+                               b_codes, b_scales, n, gsf_a, gsf_b, 0, bias, out, splits, partial, a16);
   if (e != hipSuccess || splits == 1) return e;
   const int64_t total = m * n;
   hipLaunchKernelGGL(gemm_skinny_reduce, dim3((uint32_t)((total + 255) / 256)), dim3(256), 0, s, partial, splits, m,
                      n, gsf_a, gsf_b, (int64_t)0, bias, out);
+  return hipGetLastError();
+}
+
+namespace {
+// The split a one-row fused launch takes with this workspace.
+int fused_splits(int64_t k, int64_t n, size_t workspace_bytes, int cus, int& waves) {
+  const DecodePlan plan = decode_plan(k, n, cus);
+  waves = plan.waves;
+  int splits = plan.splits;
+  if (splits > 1 && workspace_bytes < (size_t)splits * (size_t)n * sizeof(float)) splits = 1;
+  return splits;
+}
+}  // namespace
+
+bool linear_decode_fused_supported(int64_t m, int64_t k, int64_t n, const void* x, const void* b_codes,
+                                   const void* b_scales, size_t workspace_bytes, int cus) {
+  if (m != 1 || k % 32 != 0 || (((uintptr_t)x | (uintptr_t)b_codes) & 15) != 0 || ((uintptr_t)b_scales & 3) != 0)
+    return false;
+  int waves;
+  const int splits = fused_splits(k, n, workspace_bytes, cus, waves);
+  const int64_t st_all = ((k + BK - 1) / BK + 1) / 2;
+  const int64_t per_block = (st_all + splits - 1) / splits;
+  return (per_block + waves - 1) / waves <= fuse_max_st(waves);   // every wave's range fits its region
+}
+
+hipError_t launch_linear_decode_fused(const uint16_t* x, int64_t k, const uint8_t* b_codes, const uint8_t* b_scales,
+                                      int64_t n, const float* gsf_x, const float* gsf_w, const uint16_t* bias,
+                                      uint16_t* out, void* workspace, size_t workspace_bytes, int cus,
+                                      hipStream_t s) {
+  int waves;
+  const int splits = fused_splits(k, n, workspace_bytes, cus, waves);
+  float* partial = splits > 1 ? static_cast<float*>(workspace) : nullptr;
+  const int64_t tiles = (n + kDecRows - 1) / kDecRows;
+  hipError_t e = launch_decode(true, true, waves, (uint32_t)(tiles * splits), s, nullptr, nullptr, 1, k, b_codes,
+                               b_scales, n, gsf_x, gsf_w, 0, bias, out, splits, partial, x);
+  if (e != hipSuccess || splits == 1) return e;
+  hipLaunchKernelGGL(gemm_skinny_reduce, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, s, partial, splits,
+                     (int64_t)1, n, gsf_x, gsf_w, (int64_t)0, bias, out);
   return hipGetLastError();
 }
 

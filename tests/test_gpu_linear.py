@@ -296,9 +296,10 @@ def test_calibration_then_static_forward():
 @pytest.mark.parametrize("m", [1, 5, 16])
 @pytest.mark.parametrize("n,k", [(1024, 5120), (300, 4128), (5120, 1024)])
 def test_static_decode_fused_quantize(m, n, k):
-    """Static scale, up to 16 rows: nvfp4_linear quantizes inside the weight-streaming GEMM;
-    bit-identical to quantizing first and running nvfp4_gemm, and within tolerance of the
-    oracle.  The scale saturates some blocks (static range below the true amax)."""
+    """Static scale, up to 16 rows (one row in a single launch, more rows through the
+    quantize pass's fp16 operand form): bit-identical to quantizing first and running
+    nvfp4_gemm, and within tolerance of the oracle.  The scale saturates some blocks
+    (static range below the true amax)."""
     x = workloads.draw("t3", (m, k), m + k, 0, 2.0)
     w = workloads.draw("normal", (n, k), 31, n, 0.02)
     bias = workloads.draw("normal", (n,), 32, n, 0.01)
@@ -316,6 +317,31 @@ def test_static_decode_fused_quantize(m, n, k):
     assert np.array_equal(codes.cpu().numpy(), r["codes"])
     bound = accumulation_bound(o.dequantize(r["codes"], r["scales"]), o.dequantize(pw, sw), r["alpha"])
     assert_gemm_close(fused.float().cpu().numpy(), r["out"], bound)
+
+
+@pytest.mark.parametrize("n,k", [(5120, 25600), (25600, 5120), (1024, 5120), (64, 16384), (8, 32), (17, 96),
+                                 (300, 1568), (4096, 49152), (5120, 16384), (5120, 16640)])
+def test_static_one_row_fused_decode(n, k):
+    """Static scale, one row: the decode GEMM's waves quantize their own K ranges of the row
+    (one launch).  Bit-identical to quantizing first and running nvfp4_gemm, codes equal to
+    the oracle's; K spans one super tile up to ranges too long for one wave's region (those
+    shapes take the two-launch path and must agree all the same)."""
+    print(f"[static one-row fused decode] n={n} k={k}", flush=True)
+    x = workloads.draw("t3", (1, k), k, 1, 2.0)
+    w = workloads.draw("normal", (n, k), 33, n, 0.02)
+    bias = workloads.draw("normal", (n,), 34, n, 0.01)
+    packed, inv_scale, gsf_w = nv().quantize_weight(w.to(DEV))
+    xf = x.float().numpy()
+    gx = o.global_sf(np.float32(0.75) * o.amax(xf))
+    gxt = torch.tensor(float(gx), dtype=torch.float32, device=DEV)
+    fused = nv().nvfp4_linear(x.to(DEV), packed, inv_scale, gsf_w, bias.to(DEV), n, gxt)
+    codes, scales, _ = nv().quantize_activation(x.to(DEV), gxt)
+    two = nv().nvfp4_gemm(codes, scales, packed, inv_scale, gxt, gsf_w, bias.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(fused, two)
+    nib, s8 = o.nvfp4_quantize(xf, gx)
+    assert np.array_equal(codes.cpu().numpy(), o.pack_codes(nib))
+    assert np.array_equal(layout_to_canonical(scales.cpu().numpy(), 1, k), s8)
 
 
 @pytest.mark.parametrize("m", [1, 2, 3, 4])
