@@ -204,23 +204,24 @@ int linear_impl(const char* fn, const void* x, int64_t segments, int64_t seg_row
     return fail(NVFP4_ERR_WORKSPACE, "%s: need a %d-byte aligned workspace of %zu bytes, got %zu", fn,
                 NVFP4_WORKSPACE_ALIGN, need, workspace_bytes);
   const LinearWorkspace ws = carve(workspace, m, k, out_features, segments, split_k);
-#ifndef NVFP4_FUSED_STATIC_DECODE
-#define NVFP4_FUSED_STATIC_DECODE 1
+  float* gsf = gsf_out != nullptr ? gsf_out : ws.gsf;   // the GEMM reads the scales where they were written
+#ifndef NVFP4_FUSED_ONE_ROW
+#define NVFP4_FUSED_ONE_ROW 1
 #endif
-  if (NVFP4_FUSED_STATIC_DECODE && global_sf_x != nullptr && rotation_group == 0 && up == nullptr &&
-      segments == 1 && gsf_out == nullptr &&
-      nvfp4::linear_decode_fused_supported(m, k, out_features, x, packed, inv_scale, ws.gemm_bytes,
-                                           nvfp4::compute_units())) {
-    // static scale, one row: quantized by the decode GEMM's waves themselves, one launch
-    Range stage("nvfp4.quantize+gemm");
+  if (NVFP4_FUSED_ONE_ROW && rotation_group == 0 && up == nullptr && segments == 1 &&
+      nvfp4::linear_decode_fused_supported(m, k, out_features, global_sf_x == nullptr, x, packed, inv_scale,
+                                           ws.gemm_bytes, nvfp4::compute_units())) {
+    // one row: quantized (and with a dynamic scale, its abs-max taken) by the decode
+    // GEMM's blocks themselves, one launch
+    Range stage(global_sf_x != nullptr ? "nvfp4.quantize+gemm" : "nvfp4.amax+quantize+gemm");
     return hip_status(nvfp4::launch_linear_decode_fused(static_cast<const uint16_t*>(x), k, packed, inv_scale,
-                                                        out_features, global_sf_x, global_sf_w,
+                                                        out_features, global_sf_x,
+                                                        global_sf_x != nullptr ? gsf_out : gsf, global_sf_w,
                                                         static_cast<const uint16_t*>(bias),
                                                         static_cast<uint16_t*>(out), ws.gemm, ws.gemm_bytes,
                                                         nvfp4::compute_units(), s),
                       fn);
   }
-  float* gsf = gsf_out != nullptr ? gsf_out : ws.gsf;   // the GEMM reads the scales where they were written
   const bool per_segment = global_sf_x == nullptr && segments > 1;
   void* xbuf = keep_product ? static_cast<uint8_t*>(workspace) + base : nullptr;
   // a few rows: the quantize pass also writes the fp16 operand form, and the decode GEMM

@@ -281,8 +281,11 @@ __device__ __forceinline__ void dec_lds_order() { asm volatile("s_waitcnt lgkmcn
 // fp16 values, or its 128 code bytes and 16 scale bytes), 2816 bytes in all instead of
 // 4608, so seven four-wave blocks fit a compute unit's LDS instead of four.
 //
-// kFuse (with kA16 and kOne: the static-scale linear at one row): a16 points at the bf16
-// row x itself and gsf_a at its static global scale.  Each wave first quantizes its K
+// kFuse (with kA16 and kOne: the linear at one row): a16 points at the bf16 row x itself.
+// kFuseStatic: gsf_a points at its static global scale.  kFuseDynamic: every block forms
+// the dynamic scale itself from the abs-max of the whole row (read from L2; the same
+// value in every block).  Block 0 stores the scale used to gsf_dst unless that is NULL;
+// the epilogue (or the split-K reduce, from gsf_dst) applies it.  Each wave first quantizes its K
 // range of x (fuse_max_st super tiles at most) with the quantize kernels' block encoder
 // and keeps the fp16 operand form in its own LDS region, bit for bit what the quantize
 // pass would have written; the slots then carry only the weight (2304 bytes).  The
@@ -293,14 +296,15 @@ __device__ __forceinline__ void dec_lds_order() { asm volatile("s_waitcnt lgkmcn
 // Super tiles of x one wave quantizes: its region is 512 bytes each.  Five four-wave
 // blocks (six super tiles) or two eight-wave blocks (eight) fit a compute unit's LDS.
 constexpr int fuse_max_st(int waves) { return waves == 8 ? 8 : 6; }
-template <bool kA16, int kDW, bool kOne, bool kFuse = false>
+constexpr int kFuseStatic = 1, kFuseDynamic = 2;
+template <bool kA16, int kDW, bool kOne, int kFuse = 0>
 __global__ void __launch_bounds__(64 * kDW)
 __attribute__((amdgpu_waves_per_eu(kFuse && kDW == 4 ? 5 : kOne && kDW == 4 ? 7 : 4))) gemm_decode_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, int64_t m, int64_t k,
     const uint8_t* __restrict__ b_codes, const uint8_t* __restrict__ b_scales, int64_t n,
     const float* __restrict__ gsf_a, const float* __restrict__ gsf_b, int64_t a_seg_rows,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ out, int splits, float* __restrict__ partial,
-    const uint16_t* __restrict__ a16) {
+    const uint16_t* __restrict__ a16, float* __restrict__ gsf_dst) {
   // direct-load instructions per super tile and wave; bytes per slot and where the
   // weight's scale words sit in it
   constexpr int kLoads = kFuse ? 3 : kOne || kA16 ? 5 : 6;
@@ -462,13 +466,37 @@ __attribute__((amdgpu_waves_per_eu(kFuse && kDW == 4 ? 5 : kOne && kDW == 4 ? 7 
   }
   issue(s0, ring[wave][0]);
   issue(s0 + 1, ring[wave][1]);
+  float gsf_x = 0.0f;   // kFuse: the activation's global scale
   if constexpr (kFuse) {
+    if constexpr (kFuse == kFuseStatic) {
+      gsf_x = *gsf_a;
+    } else {
+      // every thread takes the abs-max of 8-value pieces of the row, then the waves'
+      // maxima meet in LDS (the ordinary loads here also wait for the direct loads above)
+      __shared__ float wave_amax[kDW];
+      float mx = 0.0f;
+      for (int64_t c = threadIdx.x; c < k / 8; c += 64 * kDW) {
+        const uint4 q = *reinterpret_cast<const uint4*>(a16 + 8 * c);
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          mx = fmaxf(mx, fabsf(__uint_as_float(w[e] << 16)));
+          mx = fmaxf(mx, fabsf(__uint_as_float(w[e] & 0xFFFF0000u)));
+        }
+      }
+      mx = wave_max(mx);
+      if (lane == 0) wave_amax[wave] = mx;
+      __syncthreads();
+      float amax = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kDW; ++w) amax = fmaxf(amax, wave_amax[w]);
+      gsf_x = global_scale_from_amax(amax);
+    }
     // x has landed once only the two super tiles' weight loads can be in flight; each
     // lane then turns 16-value blocks of it into their fp16 operand form in place (a
     // block's 32 bf16 bytes become its 32 fp16 bytes); blocks past the end of the row
     // are zero
     dec_wait<2 * kLoads>();
-    const float gsf_x = *gsf_a;
     const int blocks = count * 16;
 #pragma unroll
     for (int h = 0; h < (fuse_max_st(kDW) * 16 + 63) / 64; ++h) {
@@ -528,7 +556,8 @@ __attribute__((amdgpu_waves_per_eu(kFuse && kDW == 4 ? 5 : kOne && kDW == 4 ? 7 
   // 16x16 MFMA output: lane holds column l16, rows 4g .. 4g+3.
   const int64_t col = n0 + l16;
   if (col >= n) return;
-  const float alpha = __fdiv_rn(1.0f, __fmul_rn(*gsf_a, *gsf_b));   // one activation scale
+  if (kFuse && gsf_dst != nullptr && blockIdx.x == 0 && lane == 0) *gsf_dst = gsf_x;
+  const float alpha = __fdiv_rn(1.0f, __fmul_rn(kFuse ? gsf_x : *gsf_a, *gsf_b));   // one activation scale
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int64_t row = 4 * g + e;
@@ -566,30 +595,35 @@ DecodePlan decode_plan(int64_t k, int64_t n, int cus) {
   return {8, (int)(sp / 2)};
 }
 
-template <bool kA16, int kDW, bool kOne, bool kFuse = false>
+template <bool kA16, int kDW, bool kOne, int kFuse = 0>
 void launch_decode_t(dim3 grid, hipStream_t s, const uint8_t* a_codes, const uint8_t* a_scales, int64_t m,
                      int64_t k, const uint8_t* b_codes, const uint8_t* b_scales, int64_t n, const float* gsf_a,
                      const float* gsf_b, int64_t a_seg_rows, const uint16_t* bias, uint16_t* out, int splits,
-                     float* partial, const uint16_t* x16) {
+                     float* partial, const uint16_t* x16, float* gsf_dst) {
   hipLaunchKernelGGL((gemm_decode_kernel<kA16, kDW, kOne, kFuse>), grid, dim3(64 * kDW), 0, s, a_codes, a_scales, m, k,
-                     b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, splits, partial, x16);
+                     b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, splits, partial, x16, gsf_dst);
 }
 
-hipError_t launch_decode(bool a16, bool fuse, int waves, uint32_t blocks, hipStream_t s, const uint8_t* a_codes,
+hipError_t launch_decode(bool a16, int fuse, int waves, uint32_t blocks, hipStream_t s, const uint8_t* a_codes,
                          const uint8_t* a_scales, int64_t m, int64_t k, const uint8_t* b_codes,
                          const uint8_t* b_scales, int64_t n, const float* gsf_a, const float* gsf_b,
                          int64_t a_seg_rows, const uint16_t* bias, uint16_t* out, int splits, float* partial,
-                         const uint16_t* x16) {
+                         const uint16_t* x16, float* gsf_dst = nullptr) {
 #ifndef NVFP4_DECODE_ONE_ROW
 #define NVFP4_DECODE_ONE_ROW 1
 #endif
   const bool one = NVFP4_DECODE_ONE_ROW && m == 1;
-  auto fn = fuse ? (waves == 8 ? launch_decode_t<true, 8, true, true> : launch_decode_t<true, 4, true, true>) : a16 ? (waves == 8 ? (one ? launch_decode_t<true, 8, true> : launch_decode_t<true, 8, false>)
-                              : (one ? launch_decode_t<true, 4, true> : launch_decode_t<true, 4, false>))
-                : (waves == 8 ? (one ? launch_decode_t<false, 8, true> : launch_decode_t<false, 8, false>)
-                              : (one ? launch_decode_t<false, 4, true> : launch_decode_t<false, 4, false>));
+  auto fn =
+      fuse == kFuseStatic    ? (waves == 8 ? launch_decode_t<true, 8, true, kFuseStatic>
+                                           : launch_decode_t<true, 4, true, kFuseStatic>)
+      : fuse == kFuseDynamic ? (waves == 8 ? launch_decode_t<true, 8, true, kFuseDynamic>
+                                           : launch_decode_t<true, 4, true, kFuseDynamic>)
+      : a16 ? (waves == 8 ? (one ? launch_decode_t<true, 8, true> : launch_decode_t<true, 8, false>)
+                          : (one ? launch_decode_t<true, 4, true> : launch_decode_t<true, 4, false>))
+            : (waves == 8 ? (one ? launch_decode_t<false, 8, true> : launch_decode_t<false, 8, false>)
+                          : (one ? launch_decode_t<false, 4, true> : launch_decode_t<false, 4, false>));
   fn(dim3(blocks), s, a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, splits,
-     partial, x16);
+     partial, x16, gsf_dst);
   return hipGetLastError();
 }
 
@@ -629,7 +663,7 @@ hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales, i
   hipError_t e;
   if (m <= 16) {
     const int64_t tiles = (n + kDecRows - 1) / kDecRows;
-    e = launch_decode(false, false, plan.waves, (uint32_t)(tiles * splits), s, a_codes, a_scales, m, k, b_codes, b_scales,
+    e = launch_decode(false, 0, plan.waves, (uint32_t)(tiles * splits), s, a_codes, a_scales, m, k, b_codes, b_scales,
                       n, gsf_a, gsf_b, a_seg_rows, bias, out, splits, partial, nullptr);
   } else if (m <= 32) {
     e = launch_mt<2>(a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, bias, a_seg_rows, out, splits, partial, s);
@@ -660,7 +694,7 @@ hipError_t launch_gemm_decode_a16(const uint16_t* a16, int64_t m, int64_t k, con
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) splits = 1;
   float* partial = splits > 1 ? static_cast<float*>(workspace) : nullptr;
   const int64_t tiles = (n + kDecRows - 1) / kDecRows;
-  hipError_t e = launch_decode(true, false, plan.waves, (uint32_t)(tiles * splits), s, nullptr, nullptr, m, k,
+  hipError_t e = launch_decode(true, 0, plan.waves, (uint32_t)(tiles * splits), s, nullptr, nullptr, m, k,
                                b_codes, b_scales, n, gsf_a, gsf_b, 0, bias, out, splits, partial, a16);
   if (e != hipSuccess || splits == 1) return e;
   const int64_t total = m * n;
@@ -680,10 +714,16 @@ int fused_splits(int64_t k, int64_t n, size_t workspace_bytes, int cus, int& wav
 }
 }  // namespace
 
-bool linear_decode_fused_supported(int64_t m, int64_t k, int64_t n, const void* x, const void* b_codes,
-                                   const void* b_scales, size_t workspace_bytes, int cus) {
+bool linear_decode_fused_supported(int64_t m, int64_t k, int64_t n, bool dynamic, const void* x,
+                                   const void* b_codes, const void* b_scales, size_t workspace_bytes, int cus) {
   if (m != 1 || k % 32 != 0 || (((uintptr_t)x | (uintptr_t)b_codes) & 15) != 0 || ((uintptr_t)b_scales & 3) != 0)
     return false;
+  // Every block of the dynamic form reads the whole row for its abs-max before its K
+  // loop starts: on large weights (many blocks, or long rows) that costs more than the
+  // separate single-launch quantize (measured, one row: gate_proj 25600 x 5120 20.8 vs
+  // 19.2 us, down_proj 5120 x 25600 23.3 vs 23.3; k_proj 1024 x 5120 5.5 vs 7.4, q_proj
+  // 8192 x 5120 8.6 vs 9.8, o_proj 5120 x 8192 9.95 vs 11.6).
+  if (dynamic && n * k > ((int64_t)1 << 26)) return false;
   int waves;
   const int splits = fused_splits(k, n, workspace_bytes, cus, waves);
   const int64_t st_all = ((k + BK - 1) / BK + 1) / 2;
@@ -692,18 +732,19 @@ bool linear_decode_fused_supported(int64_t m, int64_t k, int64_t n, const void* 
 }
 
 hipError_t launch_linear_decode_fused(const uint16_t* x, int64_t k, const uint8_t* b_codes, const uint8_t* b_scales,
-                                      int64_t n, const float* gsf_x, const float* gsf_w, const uint16_t* bias,
-                                      uint16_t* out, void* workspace, size_t workspace_bytes, int cus,
-                                      hipStream_t s) {
+                                      int64_t n, const float* gsf_x, float* gsf_used, const float* gsf_w,
+                                      const uint16_t* bias, uint16_t* out, void* workspace, size_t workspace_bytes,
+                                      int cus, hipStream_t s) {
+  if (gsf_x == nullptr && gsf_used == nullptr) return hipErrorInvalidValue;   // the reduce reads the scale there
   int waves;
   const int splits = fused_splits(k, n, workspace_bytes, cus, waves);
   float* partial = splits > 1 ? static_cast<float*>(workspace) : nullptr;
   const int64_t tiles = (n + kDecRows - 1) / kDecRows;
-  hipError_t e = launch_decode(true, true, waves, (uint32_t)(tiles * splits), s, nullptr, nullptr, 1, k, b_codes,
-                               b_scales, n, gsf_x, gsf_w, 0, bias, out, splits, partial, x);
+  hipError_t e = launch_decode(true, gsf_x != nullptr ? kFuseStatic : kFuseDynamic, waves, (uint32_t)(tiles * splits), s, nullptr, nullptr, 1, k, b_codes,
+                               b_scales, n, gsf_x, gsf_w, 0, bias, out, splits, partial, x, gsf_used);
   if (e != hipSuccess || splits == 1) return e;
   hipLaunchKernelGGL(gemm_skinny_reduce, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, s, partial, splits,
-                     (int64_t)1, n, gsf_x, gsf_w, (int64_t)0, bias, out);
+                     (int64_t)1, n, gsf_x != nullptr ? gsf_x : gsf_used, gsf_w, (int64_t)0, bias, out);
   return hipGetLastError();
 }
 

@@ -107,15 +107,18 @@ hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales, i
 // weight-streaming kernel: each block quantizes its K range of the bf16 rows x [m][k]
 // into LDS (same codes and scales as launch_quantize) instead of a separate pass.
 // Needs the workspace of gemm_skinny_workspace_bytes (hipErrorInvalidValue without).
-// The static-scale linear at one activation row in one launch: each wave of the decode
-// GEMM quantizes its K range of the bf16 row itself (bit-identical to the quantize pass
-// then the GEMM).  Needs the split-K partials of gemm_workspace_bytes when the decode
-// plan splits K, else runs unsplit while every wave's range fits its LDS region.
-bool linear_decode_fused_supported(int64_t m, int64_t k, int64_t n, const void* x, const void* b_codes,
-                                   const void* b_scales, size_t workspace_bytes, int cus);
+// The linear at one activation row in one launch: each wave of the decode GEMM quantizes
+// its K range of the bf16 row itself (bit-identical to the quantize pass then the GEMM).
+// gsf_x: the static scale, or NULL for the dynamic one, which every block forms from the
+// row's abs-max.  gsf_used (NULL allowed only with a static scale) receives the scale
+// used.  Needs the split-K partials of gemm_workspace_bytes when the decode plan splits
+// K, else runs unsplit while every wave's range fits its LDS region.
+bool linear_decode_fused_supported(int64_t m, int64_t k, int64_t n, bool dynamic, const void* x,
+                                   const void* b_codes, const void* b_scales, size_t workspace_bytes, int cus);
 hipError_t launch_linear_decode_fused(const uint16_t* x, int64_t k, const uint8_t* b_codes, const uint8_t* b_scales,
-                                      int64_t n, const float* gsf_x, const float* gsf_w, const uint16_t* bias,
-                                      uint16_t* out, void* workspace, size_t workspace_bytes, int cus, hipStream_t s);
+                                      int64_t n, const float* gsf_x, float* gsf_used, const float* gsf_w,
+                                      const uint16_t* bias, uint16_t* out, void* workspace, size_t workspace_bytes,
+                                      int cus, hipStream_t s);
 
 // Workspace the GEMM dispatcher can use for an [m, k] x [n, k] product (0 if none).
 size_t gemm_workspace_bytes(int64_t m, int64_t k, int64_t n);

@@ -344,6 +344,50 @@ def test_static_one_row_fused_decode(n, k):
     assert np.array_equal(layout_to_canonical(scales.cpu().numpy(), 1, k), s8)
 
 
+@pytest.mark.parametrize("n,k", [(5120, 25600), (25600, 5120), (1024, 5120), (64, 16384), (8, 32), (17, 96),
+                                 (300, 1568), (4096, 49152), (5120, 16384), (5120, 16640)])
+def test_dynamic_one_row_fused_decode(n, k):
+    """Dynamic scale, one row: every decode block takes the row's abs-max itself, then its
+    waves quantize their K ranges (one launch).  Bit-identical to the dynamic quantize then
+    nvfp4_gemm; the scale used (reported through the segmented call) and the codes equal
+    the oracle's."""
+    print(f"[dynamic one-row fused decode] n={n} k={k}", flush=True)
+    x = workloads.draw("t3", (1, k), k, 2, 2.0)
+    w = workloads.draw("normal", (n, k), 35, n, 0.02)
+    bias = workloads.draw("normal", (n,), 36, n, 0.01)
+    packed, inv_scale, gsf_w = nv().quantize_weight(w.to(DEV))
+    xd = x.to(DEV)
+    fused = nv().nvfp4_linear(xd, packed, inv_scale, gsf_w, bias.to(DEV), n)
+    codes, scales, gsf = nv().quantize_activation(xd, None)
+    two = nv().nvfp4_gemm(codes, scales, packed, inv_scale, gsf, gsf_w, bias.to(DEV))
+    used = torch.full((1,), -1.0, dtype=torch.float32, device=DEV)
+    seg = nv().nvfp4_linear_segmented(xd, 1, packed, inv_scale, gsf_w, bias.to(DEV), n, gsf_out=used)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, two) and torch.equal(seg, fused)
+    xf = x.float().numpy()
+    gx = o.global_sf(o.amax(xf))
+    assert np.float32(gsf.item()) == gx and np.float32(used.item()) == gx
+    nib, s8 = o.nvfp4_quantize(xf, gx)
+    assert np.array_equal(codes.cpu().numpy(), o.pack_codes(nib))
+    assert np.array_equal(layout_to_canonical(scales.cpu().numpy(), 1, k), s8)
+
+
+@pytest.mark.parametrize("n,k", [(1024, 5120), (64, 16384)])
+def test_dynamic_one_row_fused_decode_zero_row(n, k):
+    """An all-zero row takes the floored scale and gives the bias alone, as the oracle."""
+    x = torch.zeros((1, k), dtype=torch.bfloat16)
+    w = workloads.draw("normal", (n, k), 37, n, 0.02)
+    bias = workloads.draw("normal", (n,), 38, n, 0.01)
+    packed, inv_scale, gsf_w = nv().quantize_weight(w.to(DEV))
+    used = torch.full((1,), -1.0, dtype=torch.float32, device=DEV)
+    out = nv().nvfp4_linear_segmented(x.to(DEV), 1, packed, inv_scale, gsf_w, bias.to(DEV), n, gsf_out=used)
+    torch.cuda.synchronize()
+    assert np.float32(used.item()) == o.global_sf(np.float32(0.0))
+    pw, sw, gw = o.quantize_weight(w.float().numpy())
+    r = o.nvfp4_linear_inference(x.float().numpy(), pw, sw, gw, bias.float().numpy())
+    assert np.array_equal(out.float().cpu().numpy(), r["out"])
+
+
 @pytest.mark.parametrize("m", [1, 2, 3, 4])
 @pytest.mark.parametrize("static,g", [(False, 0), (True, 0), (False, 16)])
 @pytest.mark.parametrize("n,k", [(1000, 4128), (5120, 1024)])
