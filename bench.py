@@ -70,15 +70,20 @@ def parse():
     return p.parse_args()
 
 
+# The sources that decide which kernels one step runs and what they do: the GEMM
+# dispatch, the pipelined GEMM, the quantize kernels and their device code.
+STEP_SOURCES = ("gemm.hip", "gemm_pipe.hip", "quantize.hip", "gemm_common.h", "nvfp4_device.h")
+
+
 def kernel_source_digest() -> str:
-    """Digest of the kernel sources: counter figures taken on other sources are stale."""
+    """Digest of the step's kernel sources: counter figures taken on other sources are
+    stale (the decode kernels, the C ABI layer and the declarations are left out)."""
     import hashlib
     d = os.path.join(ROOT, "nvfp4_w4a4_quantized_global_amd", "csrc")
     h = hashlib.sha256()
-    for name in sorted(os.listdir(d)):
-        if name.endswith((".hip", ".h")):
-            with open(os.path.join(d, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in STEP_SOURCES:
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 

@@ -92,6 +92,18 @@ def test_decode_rows_with_rotation():
     assert_gemm_close(got.float().cpu().numpy(), r, bound)
 
 
+def test_one_row_single_launch():
+    # one row (the decode GEMM quantizes the row itself), dynamic then static scale; the
+    # dynamic scale lands in the scratch for the epilogue and the split-K reduce
+    x, w, b = _case(1, 5120, 1024, 45)
+    for gsf_x in (None, 30.0):
+        print(f"no-alloc: [1, 5120] x [1024, 5120], scale {gsf_x}", flush=True)
+        got, ref = _run_pair(x, w, b, gsf_x=gsf_x)
+        assert torch.equal(got, ref)
+        r, bound = _oracle_rows(x, w, b, np.arange(1), gsf_x=gsf_x)
+        assert_gemm_close(got.float().cpu().numpy(), r, bound)
+
+
 @pytest.mark.slow
 def test_unsplit_when_only_the_codes_fit():
     # down_proj shape: the split-K partials (67 MB) do not fit beside the codes, so the
