@@ -285,14 +285,15 @@ __device__ __forceinline__ void dec_lds_order() { asm volatile("s_waitcnt lgkmcn
 // kFuseStatic: gsf_a points at its static global scale.  kFuseDynamic: every block forms
 // the dynamic scale itself from the abs-max of the whole row (read from L2; the same
 // value in every block).  Block 0 stores the scale used to gsf_dst unless that is NULL;
-// the epilogue (or the split-K reduce, from gsf_dst) applies it.  Each wave first quantizes its K
-// range of x (fuse_max_st super tiles at most) with the quantize kernels' block encoder
-// and keeps the fp16 operand form in its own LDS region, bit for bit what the quantize
-// pass would have written; the slots then carry only the weight (2304 bytes).  The
-// linear is one launch instead of two.
+// the epilogue, or the split-K reduce (from gsf_dst), applies it.  Each wave loads its K
+// range of x (fuse_max_st super tiles at most) into its own LDS region by direct loads
+// and turns it there into the fp16 operand form with the quantize kernels' block
+// encoder, bit for bit what the quantize pass would have written; the slots then carry
+// only the weight (2304 bytes).  The linear is one launch instead of two.
 //
 // Four waves per SIMD (seven for four-wave blocks with kOne, five with kFuse) bound the
 // registers.
+//
 // Super tiles of x one wave quantizes: its region is 512 bytes each.  Five four-wave
 // blocks (six super tiles) or two eight-wave blocks (eight) fit a compute unit's LDS.
 constexpr int fuse_max_st(int waves) { return waves == 8 ? 8 : 6; }
@@ -311,7 +312,7 @@ __attribute__((amdgpu_waves_per_eu(kFuse && kDW == 4 ? 5 : kOne && kDW == 4 ? 7 
   constexpr int kSlot = kFuse ? 2048 + 256 : kOne ? 2048 + 512 + 256 : kDecSlot;
   constexpr int kOffBS = kFuse ? 2048 : kOne ? 2560 : 4096;
   static_assert(kDW == 4 || kDW == 8, "waves per block");
-  static_assert(!kFuse || (kA16 && kOne), "the fused static-scale row is a one-row fp16 operand");
+  static_assert(!kFuse || (kA16 && kOne), "the fused row is a one-row fp16 operand");
   __shared__ __attribute__((aligned(16))) uint8_t ring[kDW][kDecDepth][kSlot];
   __shared__ __attribute__((aligned(16))) uint8_t arow[kFuse ? kDW : 1][kFuse ? fuse_max_st(kDW) * 512 : 16];
 
