@@ -372,6 +372,30 @@ def test_dynamic_one_row_fused_decode(n, k):
     assert np.array_equal(layout_to_canonical(scales.cpu().numpy(), 1, k), s8)
 
 
+@pytest.mark.parametrize("static", [False, True])
+@pytest.mark.parametrize("n,k", [(1024, 5120), (64, 16384), (5120, 8192)])
+def test_one_row_fused_decode_without_bias(n, k, static):
+    """The one-launch linear without a bias (split and unsplit plans, four- and eight-wave
+    blocks) equals the quantize pass plus nvfp4_gemm bit for bit, and the oracle within
+    the GEMM tolerance."""
+    x = workloads.draw("normal", (1, k), k, 3, 1.0)
+    w = workloads.draw("normal", (n, k), 39, n, 0.02)
+    packed, inv_scale, gsf_w = nv().quantize_weight(w.to(DEV))
+    xf = x.float().numpy()
+    gx = o.global_sf(np.float32(0.9) * o.amax(xf)) if static else None
+    gxt = None if gx is None else torch.tensor(float(gx), dtype=torch.float32, device=DEV)
+    fused = nv().nvfp4_linear(x.to(DEV), packed, inv_scale, gsf_w, None, n, gxt)
+    codes, scales, used = nv().quantize_activation(x.to(DEV), gxt)
+    two = nv().nvfp4_gemm(codes, scales, packed, inv_scale, used, gsf_w, None)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, two)
+    pw, sw, gw = o.quantize_weight(w.float().numpy())
+    r = o.nvfp4_linear_inference(xf, pw, sw, gw, None, gx)
+    assert np.array_equal(codes.cpu().numpy(), r["codes"])
+    bound = accumulation_bound(o.dequantize(r["codes"], r["scales"]), o.dequantize(pw, sw), r["alpha"])
+    assert_gemm_close(fused.float().cpu().numpy(), r["out"], bound)
+
+
 @pytest.mark.parametrize("n,k", [(1024, 5120), (64, 16384)])
 def test_dynamic_one_row_fused_decode_zero_row(n, k):
     """An all-zero row takes the floored scale and gives the bias alone, as the oracle."""
