@@ -284,13 +284,11 @@ hipError_t launch_cfg(const uint8_t* a_codes, const uint8_t* a_scales, int64_t m
                       const uint16_t* bias,
                       uint16_t* out, int64_t b_srows, int64_t ldo, int aligned16, hipStream_t s) {
   using C = Cfg<WM, WN, TM, TN>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<WM, WN, TM, TN>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static bool attr_set[kMaxDevices] = {};
+  if (hipError_t e = set_dynamic_lds_once(reinterpret_cast<const void*>(&gemm_kernel<WM, WN, TM, TN>), C::kLds,
+                                          attr_set);
+      e != hipSuccess)
+    return e;
   const int tiles_m = (int)((m + C::BM - 1) / C::BM);
   const int tiles_n = (int)((n + C::BN - 1) / C::BN);
   hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN>), dim3(tiles_m * tiles_n), dim3(C::kThreads), C::kLds, s, a_codes,
@@ -319,10 +317,21 @@ hipError_t launch_generic(const uint8_t* a_codes, const uint8_t* a_scales, int64
 
 }  // namespace
 
-int compute_units() {
-  static int cached[64] = {0};
+hipError_t set_dynamic_lds_once(const void* kernel, int bytes, bool (&done)[kMaxDevices]) {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (done[dev]) return hipSuccess;
+  if (hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes); e != hipSuccess)
+    return e;
+  done[dev] = true;
+  return hipSuccess;
+}
+
+int compute_units() {
+  static int cached[kMaxDevices] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
   if (cached[dev] == 0) {
     int cu = 0;
     if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0) cu = 256;

@@ -542,13 +542,11 @@ hipError_t launch_split_tail(const PipePlan& p, int sub, const uint8_t* a_codes,
                              const float* gsf_b, int64_t a_seg_rows, const uint16_t* bias, uint16_t* out,
                              float* partial, hipStream_t s) {
   constexpr int kLds = Geo<kTM>::kLds;
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_pipe_kernel<true, kTM>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static bool attr_set[kMaxDevices] = {};
+  if (hipError_t e = set_dynamic_lds_once(reinterpret_cast<const void*>(&gemm_pipe_kernel<true, kTM>), kLds,
+                                          attr_set);
+      e != hipSuccess)
+    return e;
   const int tm = (int)p.tiles_m, tn = (int)p.tiles_n;
   const int64_t units = p.rest * sub;
   hipLaunchKernelGGL((gemm_pipe_kernel<true, kTM>), dim3((uint32_t)(units * p.splits)), dim3(256), kLds, s, a_codes,
@@ -567,13 +565,11 @@ hipError_t launch_plan(const PipePlan& p, const uint8_t* a_codes, const uint8_t*
                        const float* gsf_b, int64_t a_seg_rows, const uint16_t* bias, uint16_t* out, float* partial,
                        hipStream_t s) {
   constexpr int kLds = Geo<kTM>::kLds;
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_pipe_kernel<false, kTM>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static bool attr_set[kMaxDevices] = {};
+  if (hipError_t e = set_dynamic_lds_once(reinterpret_cast<const void*>(&gemm_pipe_kernel<false, kTM>), kLds,
+                                          attr_set);
+      e != hipSuccess)
+    return e;
   const int tm = (int)p.tiles_m, tn = (int)p.tiles_n;
   if (p.full > 0) {
     hipLaunchKernelGGL((gemm_pipe_kernel<false, kTM>), dim3((uint32_t)p.full), dim3(256), kLds, s, a_codes, a_scales,

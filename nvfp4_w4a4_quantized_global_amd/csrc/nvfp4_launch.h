@@ -8,6 +8,13 @@
 
 namespace nvfp4 {
 
+// Devices the library keeps per-device state for (compute-unit counts, kernel attributes).
+constexpr int kMaxDevices = 64;
+
+// Raises a kernel's dynamic LDS limit to `bytes` on the current device, once per device
+// (`done` is the caller's per-kernel record); a no-op after the first call there.
+hipError_t set_dynamic_lds_once(const void* kernel, int bytes, bool (&done)[kMaxDevices]);
+
 // Upper bound on the number of per-block partial maxima of the amax pass, and on the
 // number of segments (row blocks with their own scale) of one call.
 constexpr int kMaxAmaxPartials = 8192;
