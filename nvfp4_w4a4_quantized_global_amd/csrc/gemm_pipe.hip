@@ -398,7 +398,8 @@ __global__ void __launch_bounds__(256, 1) gemm_pipe_kernel(
       if (row < m) {
         uint16_t* o = out_i + 4 * p * ldo;
         if (vec_store) {
-          *reinterpret_cast<uint4*>(o) = make_uint4(w[0], w[1], w[2], w[3]);
+          typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+          __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4*>(o));
         } else if (col < n) {
           const uint64_t lo = ((uint64_t)w[1] << 32) | w[0], hi = ((uint64_t)w[3] << 32) | w[2];
           const int cnt = n - col < 8 ? (int)(n - col) : 8;
