@@ -614,15 +614,18 @@ hipError_t launch_decode(bool a16, int fuse, int waves, uint32_t blocks, hipStre
 #define NVFP4_DECODE_ONE_ROW 1
 #endif
   const bool one = NVFP4_DECODE_ONE_ROW && m == 1;
-  auto fn =
-      fuse == kFuseStatic    ? (waves == 8 ? launch_decode_t<true, 8, true, kFuseStatic>
-                                           : launch_decode_t<true, 4, true, kFuseStatic>)
-      : fuse == kFuseDynamic ? (waves == 8 ? launch_decode_t<true, 8, true, kFuseDynamic>
-                                           : launch_decode_t<true, 4, true, kFuseDynamic>)
-      : a16 ? (waves == 8 ? (one ? launch_decode_t<true, 8, true> : launch_decode_t<true, 8, false>)
-                          : (one ? launch_decode_t<true, 4, true> : launch_decode_t<true, 4, false>))
-            : (waves == 8 ? (one ? launch_decode_t<false, 8, true> : launch_decode_t<false, 8, false>)
-                          : (one ? launch_decode_t<false, 4, true> : launch_decode_t<false, 4, false>));
+  using Launch = decltype(&launch_decode_t<false, 4, false>);
+  // [activation form][one row][eight waves]; the fused forms are one-row fp16 only
+  static constexpr Launch kPlain[2][2][2] = {
+      {{launch_decode_t<false, 4, false>, launch_decode_t<false, 8, false>},
+       {launch_decode_t<false, 4, true>, launch_decode_t<false, 8, true>}},
+      {{launch_decode_t<true, 4, false>, launch_decode_t<true, 8, false>},
+       {launch_decode_t<true, 4, true>, launch_decode_t<true, 8, true>}}};
+  static constexpr Launch kFused[2][2] = {
+      {launch_decode_t<true, 4, true, kFuseStatic>, launch_decode_t<true, 8, true, kFuseStatic>},
+      {launch_decode_t<true, 4, true, kFuseDynamic>, launch_decode_t<true, 8, true, kFuseDynamic>}};
+  const int w8 = waves == 8 ? 1 : 0;
+  const Launch fn = fuse != 0 ? kFused[fuse == kFuseDynamic ? 1 : 0][w8] : kPlain[a16 ? 1 : 0][one ? 1 : 0][w8];
   fn(dim3(blocks), s, a_codes, a_scales, m, k, b_codes, b_scales, n, gsf_a, gsf_b, a_seg_rows, bias, out, splits,
      partial, x16, gsf_dst);
   return hipGetLastError();
