@@ -413,7 +413,7 @@ def test_dynamic_one_row_fused_decode_zero_row(n, k):
 
 
 @pytest.mark.parametrize("m", [1, 2, 3, 4])
-@pytest.mark.parametrize("static,g", [(False, 0), (True, 0), (False, 16)])
+@pytest.mark.parametrize("static,g", [(False, 0), (True, 0), (False, 16), (True, 16)])
 @pytest.mark.parametrize("n,k", [(1000, 4128), (5120, 1024)])
 def test_fp16_activation_decode_equals_codes_path(m, static, g, n, k):
     """At most four rows nvfp4_linear hands the decode GEMM the quantized activation in
