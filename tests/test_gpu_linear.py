@@ -176,6 +176,31 @@ def test_decode_sweep_sampled_columns(name, m):
     assert_gemm_close(out.float().cpu().numpy()[:, cols], r["out"], bound)
 
 
+@pytest.mark.parametrize("name", [p[0] for p in workloads.QWEN3_PROJECTIONS])
+def test_decode_sweep_static_one_row(name):
+    """One row of the small-M sweep with a static scale below the row's abs-max (some
+    blocks saturate): the single-launch linear at full size, on 160 sampled output
+    columns (plus the last 16) against the oracle."""
+    print(f"[decode sweep, static] M=1 {name}", flush=True)
+    w, packed, inv_scale, gsf_w = _decode_weight(name)
+    n, k = w.shape
+    x = workloads.small_m_input(1, name)
+    xf = x.float().numpy()
+    gx = o.global_sf(np.float32(0.8) * o.amax(xf))
+    gxt = torch.tensor(float(gx), dtype=torch.float32, device=DEV)
+    out = nv().nvfp4_linear(x.to(DEV), packed, inv_scale, gsf_w, None, n, gxt)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7 * n + k)
+    cols = np.unique(np.concatenate([rng.choice(n, 160, replace=False), np.arange(n - 16, n)]))
+    wf = w.float().numpy()
+    gw = o.global_sf(o.amax(wf))
+    nib, sw = o.nvfp4_quantize(wf[cols], gw)
+    pw = o.pack_codes(nib)
+    r = o.nvfp4_linear_inference(xf, pw, sw, gw, None, gx)
+    bound = accumulation_bound(o.dequantize(r["codes"], r["scales"]), o.dequantize(pw, sw), r["alpha"])
+    assert_gemm_close(out.float().cpu().numpy()[:, cols], r["out"], bound)
+
+
 def _segmented_inputs(segments, seg_rows, k, seed):
     """Row blocks with very different magnitudes, so per-segment scales differ."""
     x = workloads.draw("t3", (segments * seg_rows, k), seed, 0)
