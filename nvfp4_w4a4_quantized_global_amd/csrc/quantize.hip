@@ -272,7 +272,9 @@ constexpr int64_t kSmallQuantValues = NVFP4_SMALL_QUANT_VALUES;
 #define NVFP4_SMALL_QUANT_BLOCKS 16
 #endif
 constexpr int kSmallBlocks = NVFP4_SMALL_QUANT_BLOCKS;
-constexpr int kSmallUnroll = 4;   // pass-1 chunks in flight per lane
+constexpr int kSmallUnroll = 4;   // pass-1 chunks in flight per lane (with a rotation)
+constexpr int kSmallRaw = (int)(kSmallQuantValues / kBlock / kSmallThreads);   // without one
+static_assert(kSmallRaw >= 1 && kSmallRaw <= 8, "bf16 chunks per lane in flight");
 
 template <bool kRotate>
 __global__ void __launch_bounds__(kSmallThreads) quantize_small_kernel(
@@ -300,6 +302,39 @@ __global__ void __launch_bounds__(kSmallThreads) quantize_small_kernel(
       for (int i = 0; i < 16; ++i) v[i] = 0.0f;
     }
     chunk_max(v);
+  } else if (!kRotate && n_chunks > kSmallUnroll * kSmallThreads) {
+    // Past one round of kSmallUnroll chunks per lane, and without a rotation, every
+    // chunk of the lane is in flight at once (at most kSmallRaw under the size
+    // threshold), kept as bf16, and the abs-max is taken on the magnitude bits, which
+    // order as the values do for every bf16 but NaN (an input with NaNs has no defined
+    // scale).  Measured, dynamic linear at 16 rows (HIP graph, one box): o_proj 18.0 ->
+    // 17.0 us, gate 27.5 -> 26.8, k 11.4 -> 10.9.
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    u16x2 m2 = {0, 0};
+    for (int64_t c0 = 0; c0 < n_chunks; c0 += kSmallRaw * kSmallThreads) {
+      uint4 r[kSmallRaw][2];
+#pragma unroll
+      for (int u = 0; u < kSmallRaw; ++u) {
+        const int64_t c = c0 + u * kSmallThreads + t;
+        if (c < n_chunks) {
+          r[u][0] = reinterpret_cast<const uint4*>(x + c * kBlock)[0];
+          r[u][1] = reinterpret_cast<const uint4*>(x + c * kBlock)[1];
+        } else {
+          r[u][0] = r[u][1] = make_uint4(0, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kSmallRaw; ++u) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t w[4] = {r[u][h].x, r[u][h].y, r[u][h].z, r[u][h].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, w[e] & 0x7FFF7FFFu));
+        }
+      }
+    }
+    mx = __uint_as_float((uint32_t)(m2.x > m2.y ? m2.x : m2.y) << 16);
   } else {
     for (int64_t c0 = 0; c0 < n_chunks; c0 += kSmallUnroll * kSmallThreads) {
       float v[kSmallUnroll][16];
