@@ -38,7 +38,7 @@ The steps, in the order ``nvfp4_linear_inference`` runs them:
    output in the activation dtype (bf16), bias added afterwards ([DEC]
    ``nvfp4_linear_inference``).
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 FP4 is E2M1 with magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}; ``FP4_E4M3_RANGE`` =
 6 * 448 = 2688; block scale ``s = E4M3_rne_satfinite(fp32(fp32(gsf*bmax)/6))``;
 code ``E2M1_rne_sat(fp32(v * fp32(gsf/s)))`` with the sign of v kept (all codes
